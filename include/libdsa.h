@@ -1,0 +1,224 @@
+/*
+ * libdsa -- the data-parallel hot path of DeepSeek Sparse Attention (DSA)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Three stages, each a HIP kernel family behind this C ABI:
+ *   1. lightning-indexer scores   I[t,s] = scale * sum_j w[t,j] * ReLU(q[t,j] . k[s])
+ *   2. per-query causal top-k     S_t = the min(k, n_t) best positions, ascending
+ *   3. sparse MLA over S_t        absorbed (MQA) form with online softmax
+ *
+ * Sources (page title, section / equation):
+ *   [G] "DeepSeek Sparse Attention DSA Architecture Guide":
+ *       "Stage 1: The Lightning Indexer" -- the ReLU score equation and item 3
+ *         (per-key separable scores; FP8 operands, item 1);
+ *       "Stage 2: Fine-Grained Token Selection" -- the TopK, gather and u_t
+ *         equations (softmax restricted to S_t);
+ *       "The Classical Multi-Head Latent Attention (MLA) Mechanism" -- the
+ *         latent + decoupled-rotary logit A_{t,s,i};
+ *       "End-to-End Implementation" -- k = min(top_k, seq_len), selected
+ *         positions re-sorted into ascending (temporal) order;
+ *       the two-stage pipeline figure (indexer -> top-k -> selective fetch ->
+ *         sparse MLA kernel).
+ *   [P] "Sparse Attention in Large Language Models: Architecture Evolution
+ *       and Engineering Practice", section 4.1 -- paged KV-cache storage.
+ *
+ * Conventions (the pages give none; these are the library's):
+ *   - Every tensor pointer is a DEVICE pointer unless stated otherwise; the
+ *     descriptor structs themselves are host memory, read during the call.
+ *   - Layouts are row-major and densely packed as written ([a,b,c]: c fastest).
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronises; every call only enqueues kernels on `stream` and returns.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation failure nothing is enqueued.  Shapes the kernels do not
+ *     implement return DSA_ERR_UNSUPPORTED.  A failed launch returns
+ *     DSA_ERR_HIP.  dsa_last_error() then describes the failure.
+ *   - Device-side preconditions are documented, not checked: batch arrays
+ *     consistent with the host-side bounds, indices in range, page ids
+ *     valid, no NaN scores.
+ *   - The library keeps no mutable global state: calls on different streams
+ *     (or threads) may run concurrently if their buffers do not overlap.
+ *
+ * Batch semantics.  Sequence b owns query rows q_seq_start[b] ..
+ * q_seq_start[b+1]-1 and a key history of k_len[b] tokens.  Its nq_b queries
+ * are the LAST nq_b tokens of that history, so query i of sequence b sits at
+ * position p = k_len[b] - nq_b + i and sees keys 0..p (causal and
+ * self-inclusive, [G] Stage 1: s <= t):  n_t = p + 1 candidates.
+ *   prefill: B = 1, nq = k_len = L (row t sees t + 1 keys);
+ *   decode:  nq_b = 1, the query sees its whole history (n = k_len[b]).
+ * Precondition: 0 <= nq_b <= k_len[b].
+ */
+#ifndef LIBDSA_H
+#define LIBDSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent args */
+  DSA_ERR_UNSUPPORTED = 2,        /* valid, but no kernel for this shape/dtype */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,        /* IEEE binary32 */
+  DSA_BF16 = 1,       /* bfloat16 */
+  DSA_FP8_E4M3 = 2    /* OCP FP8 E4M3 (bias 7, max 448, 0x7F/0xFF NaN) + fp32 per-token scale */
+} dsa_dtype_t;
+
+/* Ragged batch of query rows.  Arrays are device memory. */
+typedef struct {
+  int32_t num_seqs;             /* B >= 1 */
+  int32_t num_queries;          /* T = q_seq_start[B] (host copy of that value) */
+  const int32_t *q_seq_start;   /* [B+1], q_seq_start[0] = 0, non-decreasing */
+  const int32_t *k_len;         /* [B], history length of each sequence */
+  int32_t max_q_per_seq;        /* host bound: >= every nq_b */
+  int32_t max_k_len;            /* host bound: >= every k_len[b] */
+} dsa_batch_t;
+
+/* Where a sequence's key rows live (indexer keys and latent cache alike). */
+typedef struct {
+  int32_t paged;                /* 0: contiguous, 1: paged */
+  /* contiguous: key s of sequence b is row k_seq_start[b] + s of a
+     [num_rows, width] array */
+  const int64_t *k_seq_start;   /* [B] device; ignored when paged */
+  /* paged: key s of sequence b is slot s % page_size of physical page
+     page_table[b * page_table_stride + s / page_size] of a
+     [num_rows(pages), page_size, width] pool ([P] section 4.1) */
+  const int32_t *page_table;    /* [B, page_table_stride] device; ignored when contiguous */
+  int32_t page_table_stride;
+  int32_t page_size;            /* tokens per page; 64 is the supported value */
+  int64_t num_rows;             /* contiguous: rows in the cache; paged: pages in the pool */
+} dsa_kv_layout_t;
+
+/* ------------------------------------------------------------------------
+ * Stage 1: lightning-indexer scores ([G] Stage 1, ReLU score equation, in
+ * its multi-head weighted form).  For every query row t and s < n_t:
+ *
+ *   scores[t*ld_scores + s] = scale * sq[t] * sk[s] *
+ *                             sum_{j<h_i} w[t*h_i+j] * ReLU(sum_{d<d_i} q[t,j,d] * k[s,d])
+ *
+ * where sq / sk are the per-token FP8 scales (1 for DSA_F32).  Because the
+ * scales are positive they factor out of the ReLU, so this equals the score
+ * of the dequantised operands.  The [T, n, h_i] per-head products are never
+ * stored.  Entries s >= n_t of each row are left untouched.
+ *   dtype   DSA_FP8_E4M3 (q_idx/k_idx are bytes, q_scale/k_scale required,
+ *           h_i % 16 == 0, d_i == 128) or DSA_F32 (scales must be NULL;
+ *           h_i <= 64, d_i <= 128).
+ *   q_idx   [T, h_i, d_i];  q_scale [T];  w [T, h_i] fp32
+ *   k_idx   contiguous [num_rows, d_i] or paged [pages, page_size, d_i];
+ *   k_scale contiguous [num_rows] or paged [pages, page_size]
+ *   scale   multiplies every score (1.0, or 1/sqrt(d_i) for the page form)
+ *   scores  [T, ld_scores] fp32, ld_scores >= max n_t (= max_k_len suffices)
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_indexer_scores(const dsa_batch_t *batch, const dsa_kv_layout_t *keys,
+                                dsa_dtype_t dtype, int32_t h_i, int32_t d_i,
+                                const void *q_idx, const float *q_scale, const float *w,
+                                const void *k_idx, const float *k_scale, float scale,
+                                float *scores, int64_t ld_scores, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2: top-k ([G] Stage 2, TopK equation; "End-to-End Implementation"
+ * for min(k, n) and ascending order).  For every query row t, writes the
+ * positions of the m = min(k, n_t) largest of scores[t, 0..n_t-1] to
+ * indices[t*k .. t*k+m-1] in ascending order and -1 to the remaining k - m
+ * slots.  Ties go to the lowest position; scores compare by value (-0 == +0).
+ * NaN scores are a precondition violation (the result is then unspecified
+ * but stays in range).  The result is deterministic.
+ *   1 <= k <= 65536.  workspace: dsa_topk_workspace_size() bytes (may be 0).
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_scores,
+                      int32_t k, int32_t *indices,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * Stage 3: sparse MLA, absorbed (MQA) form ([G] Stage 2, gather and u_t
+ * equations; logit of the classical MLA section).  For query row t and head
+ * h, with J = { indices[t*k + j] : j < k, indices[t*k + j] >= 0 }:
+ *
+ *   z_s      = sm_scale * sum_{d<d_qk} q[t,h,d] * kv[s,d]        (s in J)
+ *   out[t,h] = sum_s softmax_J(z)_s * kv[s, 0..d_v-1]
+ *   lse[t,h] = log sum_s exp(z_s)                                (natural log)
+ *
+ * The key row of a token is [c^KV (d_v) ; k^R (d_qk - d_v)]: one row shared
+ * by every head; the value is its first d_v entries.  An empty J gives
+ * out = 0 and lse = -inf.  Indices are positions within the query's
+ * sequence (as written by dsa_topk) and must be < n_t.
+ *   dtype  DSA_BF16 (q, kv, out bf16; heads % 16 == 0, d_qk == 576,
+ *          d_v == 512) or DSA_F32 (heads <= 64, d_qk <= 128, d_v <= d_qk).
+ *   q      [T, heads, d_qk];  kv contiguous [num_rows, d_qk] or paged
+ *          [pages, page_size, d_qk];  indices [T, k] int32
+ *   out    [T, heads, d_v] (dtype);  lse [T, heads] fp32, may be NULL
+ *   workspace: dsa_sparse_mla_workspace_size() bytes (split partials for
+ *          small batches; may be 0).
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_sparse_mla_fwd(const dsa_batch_t *batch, const dsa_kv_layout_t *kv_layout,
+                                dsa_dtype_t dtype, int32_t heads, int32_t d_qk, int32_t d_v,
+                                const void *q, const void *kv, const int32_t *indices,
+                                int32_t k, float sm_scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+dsa_status_t dsa_sparse_mla_workspace_size(const dsa_batch_t *batch, dsa_dtype_t dtype,
+                                           int32_t heads, int32_t d_qk, int32_t d_v,
+                                           int32_t k, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * The whole path: indexer -> top-k -> sparse MLA, in the order of [G]'s
+ * pipeline figure, enqueued back to back on one stream.  Both caches use the
+ * same layout descriptor.  `scores` / `indices` may be NULL, in which case
+ * they live in the workspace; otherwise the caller keeps them.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  dsa_batch_t batch;
+  dsa_kv_layout_t layout;
+  /* indexer */
+  dsa_dtype_t index_dtype;
+  int32_t h_i, d_i;
+  const void *q_idx;
+  const float *q_scale;
+  const float *w;
+  const void *k_idx;
+  const float *k_scale;
+  float index_scale;
+  /* selection */
+  int32_t top_k;
+  float *scores;              /* [T, ld_scores] or NULL */
+  int64_t ld_scores;          /* used when scores != NULL */
+  int32_t *indices;           /* [T, top_k] or NULL */
+  /* attention */
+  dsa_dtype_t mla_dtype;
+  int32_t heads, d_qk, d_v;
+  const void *q;
+  const void *kv;
+  float sm_scale;
+  void *out;
+  float *lse;                 /* may be NULL */
+} dsa_forward_args_t;
+
+dsa_status_t dsa_forward(const dsa_forward_args_t *args, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+dsa_status_t dsa_forward_workspace_size(const dsa_forward_args_t *args, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * ---------------------------------------------------------------------- */
+const char *dsa_status_string(dsa_status_t status);   /* static string */
+const char *dsa_last_error(void);   /* detail of this thread's last failure, "" if none */
+int32_t dsa_abi_version(void);      /* == DSA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDSA_H */

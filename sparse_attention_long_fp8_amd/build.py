@@ -1,0 +1,72 @@
+"""Build libdsa.so (and the test-only MFMA probe library) for gfx950 with hipcc.
+
+Usage: python -m sparse_attention_long_fp8_amd.build [-v]
+The libraries are written next to this file, so they travel with the tree.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+INCLUDE = os.path.join(ROOT, "include")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed fp32 instructions are disabled: hipcc -O3 would otherwise emit them
+# from ordinary float code.
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+
+LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "libdsa.cpp"]
+PROBE_SOURCES = ["probe.hip"]
+
+LIB_PATH = os.path.join(PKG, "libdsa.so")
+PROBE_PATH = os.path.join(PKG, "libdsa_probe.so")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature: drop that note
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError("command failed: %s\n%s" % (" ".join(cmd), err))
+    if verbose and err.strip():
+        print(err)
+
+
+def _compile(src, verbose):
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    _run([HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    return obj
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link both libraries; returns libdsa.so's path."""
+    srcs = LIB_SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in LIB_SOURCES], LIB_PATH, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_PATH, verbose)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the libdsa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// Batch description as the kernels see it (device arrays).
+struct BatchDev {
+  int32_t num_seqs;
+  const int32_t *q_seq_start;  // [B+1]
+  const int32_t *k_len;        // [B]
+};
+
+// Key addressing: contiguous rows or 64-token pages.
+struct KeysDev {
+  int32_t paged;
+  const int64_t *k_seq_start;  // [B] (contiguous)
+  const int32_t *page_table;   // [B, stride] (paged)
+  int32_t stride;
+};
+
+constexpr int kPageShift = 6;  // 64-token pages
+constexpr int kPageSize = 1 << kPageShift;
+
+// Sequence that owns query row t: the largest b with q_seq_start[b] <= t.
+__device__ __forceinline__ int seq_of_row(const BatchDev &bt, int t) {
+  int lo = 0, hi = bt.num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (bt.q_seq_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Query row t of sequence b sits at p = k_len[b] - nq_b + (t - q_seq_start[b])
+// and has n = p + 1 causal candidates (itself included).
+__device__ __forceinline__ int candidates_of_row(const BatchDev &bt, int b, int t) {
+  int q0 = bt.q_seq_start[b];
+  int nq = bt.q_seq_start[b + 1] - q0;
+  return bt.k_len[b] - nq + (t - q0) + 1;
+}
+
+// Flat row (contiguous row, or page * 64 + slot of the pool) of key s of sequence b.
+__device__ __forceinline__ int64_t key_row(const KeysDev &kd, int b, int s) {
+  if (!kd.paged) return kd.k_seq_start[b] + s;
+  int page = kd.page_table[(int64_t)b * kd.stride + (s >> kPageShift)];
+  return ((int64_t)page << kPageShift) + (s & (kPageSize - 1));
+}
+
+// Order-preserving map float -> uint32 (a > b  <=>  key(a) > key(b));
+// -0 is folded onto +0 so that they compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Exclusive count of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace dsa

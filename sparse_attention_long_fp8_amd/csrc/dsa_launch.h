@@ -1,0 +1,42 @@
+// Internal launcher entry points of the libdsa kernels (C++ linkage; the
+// public C ABI lives in include/libdsa.h and is implemented in libdsa.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct BatchDev;
+struct KeysDev;
+
+hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_queries,
+                              int max_k_len, int h_i, int d_i, const float *q, const float *w,
+                              const float *k, float scale, float *scores, int64_t ld,
+                              hipStream_t stream);
+
+hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_queries,
+                              int max_k_len, int h_i, const uint8_t *q, const float *q_scale,
+                              const float *w, const uint8_t *k, const float *k_scale, float scale,
+                              float *scores, int64_t ld, hipStream_t stream);
+
+hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
+                       int k, int32_t *indices, hipStream_t stream);
+
+// Split count the bf16 sparse-MLA kernel uses for this many query rows
+// (1 = no split, no workspace).
+int mla_bf16_splits(int num_queries, int heads, int k);
+size_t mla_bf16_workspace_bytes(int num_queries, int heads, int d_v, int k);
+
+hipError_t launch_mla_f32(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
+                          int d_qk, int d_v, const float *q, const float *kv,
+                          const int32_t *indices, int k, float sm_scale, float *out, float *lse,
+                          hipStream_t stream);
+
+hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
+                           const void *q, const void *kv, const int32_t *indices, int k,
+                           float sm_scale, void *out, float *lse, void *workspace,
+                           hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,170 @@
+// Lightning-indexer score kernels (gfx950).
+//
+// Computes, for every query row t and causal candidate s < n_t,
+//   score[t,s] = scale * sq[t] * sk[s] * sum_j w[t,j] * ReLU(q[t,j,:] . k[s,:])
+// ("DeepSeek Sparse Attention DSA Architecture Guide", "Stage 1: The
+// Lightning Indexer": ReLU score equation, in its multi-head weighted form;
+// FP8 operands per item 1 of that section).  The per-token FP8 scales are
+// positive, so they factor out of the ReLU and are applied once per score;
+// the FP8 x FP8 products are exact in the fp32 MFMA accumulator.  The
+// [T, n, H_I] per-head products only ever live in registers.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+// --------------------------------------------------------------------------
+// fp32 path (small shapes: h_i <= 64, d_i <= 128).  One thread per (t, s).
+// --------------------------------------------------------------------------
+constexpr int kIdxF32Threads = 256;
+
+__global__ __launch_bounds__(kIdxF32Threads) void indexer_f32_kernel(
+    BatchDev bt, KeysDev kd, int h_i, int d_i, const float *__restrict__ q,
+    const float *__restrict__ w, const float *__restrict__ k, float scale,
+    float *__restrict__ scores, int64_t ld) {
+  __shared__ float q_s[64 * 128];
+  __shared__ float w_s[64];
+  const int t = blockIdx.y;
+  const int b = seq_of_row(bt, t);
+  const int n = candidates_of_row(bt, b, t);
+  const int s0 = blockIdx.x * kIdxF32Threads;
+  if (s0 >= n) return;  // uniform over the block
+  const float *qt = q + (int64_t)t * h_i * d_i;
+  for (int i = threadIdx.x; i < h_i * d_i; i += kIdxF32Threads) q_s[i] = qt[i];
+  if (threadIdx.x < h_i) w_s[threadIdx.x] = w[(int64_t)t * h_i + threadIdx.x];
+  __syncthreads();
+  const int s = s0 + threadIdx.x;
+  if (s >= n) return;
+  const float *kr = k + key_row(kd, b, s) * d_i;
+  float acc = 0.f;
+  for (int j = 0; j < h_i; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < d_i; ++d) dot = fmaf(q_s[j * d_i + d], kr[d], dot);
+    acc = fmaf(w_s[j], fmaxf(dot, 0.f), acc);
+  }
+  scores[(int64_t)t * ld + s] = scale * acc;
+}
+
+// --------------------------------------------------------------------------
+// FP8 E4M3 path, d_i = 128, h_i = 32 * MT.
+//
+// Per query row, the heads are the M dimension of a 32x32x64 FP8 MFMA and
+// 32 keys its N dimension: a wave multiplies the row's [h_i x 128] query
+// block (kept in registers for the whole launch) by a [128 x 32] key tile
+// read straight from HBM, two K-steps per 32 heads.  Lane l supplies
+// operand row/column l % 32 and the 32-byte K-slice 32 * (l / 32) of each
+// 64-wide K-step, identically for both operands, so the products pair
+// matching d.  The accumulator lane holds column l % 32 (its key) and rows
+// 8 * (i / 4) + 4 * (l / 32) + i % 4 (its heads); ReLU and the head weight
+// are applied there, and the two half-waves' partial sums are added with one
+// cross-lane swap.  Every key byte is read once per query row.
+// --------------------------------------------------------------------------
+constexpr int kIdxThreads = 256;  // 4 waves
+constexpr int kIdxTile = 32;      // keys per MFMA tile
+
+template <int MT>
+__global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
+    BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const float *__restrict__ w, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld,
+    int keys_per_block) {
+  constexpr int H = 32 * MT;
+  const int t = blockIdx.y;
+  const int b = seq_of_row(bt, t);
+  const int n = candidates_of_row(bt, b, t);
+  const int s_begin = blockIdx.x * keys_per_block;
+  if (s_begin >= n) return;
+  const int s_end = min(n, s_begin + keys_per_block);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // query operand: head 32*mt + col, bytes [64*ks + 32*half, +32)
+  v8i a[MT][2];
+  const uint8_t *qt = q + (int64_t)t * H * 128;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      a[mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
+  // head weights of the accumulator rows this lane holds
+  float wr[MT][16];
+  const float *wt = w + (int64_t)t * H;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[mt][i] = wt[32 * mt + 8 * (i / 4) + 4 * half + (i % 4)];
+  const float row_scale = q_scale[t] * scale;
+  float *out = scores + (int64_t)t * ld;
+
+  int s0 = s_begin + kIdxTile * wave;
+  v8i nb0 = {}, nb1 = {};
+  float nks = 0.f;
+  auto load_tile = [&](int s_tile, v8i &b0, v8i &b1, float &ksc) {
+    int s = min(s_tile + col, n - 1);  // clamp: stays inside the history
+    int64_t row = key_row(kd, b, s);
+    const uint8_t *kr = k + row * 128 + 32 * half;
+    b0 = *(const v8i *)(kr);
+    b1 = *(const v8i *)(kr + 64);
+    ksc = k_scale[row];
+  };
+  if (s0 < s_end) load_tile(s0, nb0, nb1, nks);
+  for (; s0 < s_end; s0 += kIdxTile * 4) {
+    v8i b0 = nb0, b1 = nb1;
+    float ksc = nks;
+    if (s0 + kIdxTile * 4 < s_end) load_tile(s0 + kIdxTile * 4, nb0, nb1, nks);
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v16f acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][0], b0, acc, 0, 0, 0, 127, 0, 127);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][1], b1, acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], fmaxf(acc[i], 0.f), sum);
+    }
+    sum += __shfl_xor(sum, 32, 64);
+    const int s = s0 + col;
+    if (half == 0 && s < s_end) out[s] = sum * row_scale * ksc;
+  }
+}
+
+// --------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------
+hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_queries,
+                              int max_k_len, int h_i, int d_i, const float *q, const float *w,
+                              const float *k, float scale, float *scores, int64_t ld,
+                              hipStream_t stream) {
+  dim3 grid((max_k_len + kIdxF32Threads - 1) / kIdxF32Threads, num_queries);
+  hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(kIdxF32Threads), 0, stream, bt, kd, h_i, d_i,
+                     q, w, k, scale, scores, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_queries,
+                              int max_k_len, int h_i, const uint8_t *q, const float *q_scale,
+                              const float *w, const uint8_t *k, const float *k_scale, float scale,
+                              float *scores, int64_t ld, hipStream_t stream) {
+  const int keys_per_block = kIdxTile * 4 * 4;  // 4 waves x 4 tiles
+  dim3 grid((max_k_len + keys_per_block - 1) / keys_per_block, num_queries);
+  switch (h_i / 32) {
+    case 1:
+      hipLaunchKernelGGL(indexer_fp8_kernel<1>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+      break;
+    case 2:
+      hipLaunchKernelGGL(indexer_fp8_kernel<2>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+      break;
+    case 4:
+      hipLaunchKernelGGL(indexer_fp8_kernel<4>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,307 @@
+// libdsa host library: argument validation, workspace sizing and kernel
+// dispatch behind the C ABI of include/libdsa.h.  Nothing here allocates,
+// frees or synchronises; every call validates first and only then enqueues.
+#include "libdsa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status_t ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+dsa_status_t check_batch(const dsa_batch_t *bt) {
+  if (!bt) return fail(DSA_ERR_INVALID_ARGUMENT, "batch is NULL");
+  if (bt->num_seqs < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+  if (bt->num_queries < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "num_queries must be >= 0");
+  if (bt->max_q_per_seq < 0 || bt->max_k_len < 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_q_per_seq / max_k_len must be >= 0");
+  if (bt->max_q_per_seq > bt->max_k_len)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "max_q_per_seq exceeds max_k_len (queries are the last tokens of their history)");
+  if (bt->num_queries > 0) {
+    if (!bt->q_seq_start || !bt->k_len) return fail(DSA_ERR_INVALID_ARGUMENT, "q_seq_start / k_len is NULL");
+    if (bt->max_k_len < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "max_k_len must be >= 1 when there are queries");
+    if ((int64_t)bt->num_queries > (int64_t)bt->num_seqs * bt->max_q_per_seq)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "num_queries exceeds num_seqs * max_q_per_seq");
+  }
+  return DSA_OK;
+}
+
+dsa_status_t check_layout(const dsa_kv_layout_t *ly, const dsa_batch_t *bt, const char *what) {
+  if (!ly) return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout is NULL", what);
+  if (ly->paged != 0 && ly->paged != 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: paged must be 0 or 1", what);
+  if (ly->num_rows < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: num_rows must be >= 1", what);
+  if (ly->paged) {
+    if (!ly->page_table) return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: page_table is NULL", what);
+    if (ly->page_size != dsa::kPageSize)
+      return fail(DSA_ERR_UNSUPPORTED, "%s layout: page_size %d (only %d is implemented)", what, ly->page_size, dsa::kPageSize);
+    const int64_t need = ((int64_t)bt->max_k_len + ly->page_size - 1) / ly->page_size;
+    if (ly->page_table_stride < need)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: page_table_stride %d < pages of max_k_len (%lld)", what,
+                  ly->page_table_stride, (long long)need);
+  } else {
+    if (!ly->k_seq_start) return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: k_seq_start is NULL", what);
+    if (ly->num_rows < bt->max_k_len)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "%s layout: num_rows %lld < max_k_len %d", what, (long long)ly->num_rows, bt->max_k_len);
+  }
+  return DSA_OK;
+}
+
+dsa::BatchDev to_dev(const dsa_batch_t *bt) { return dsa::BatchDev{bt->num_seqs, bt->q_seq_start, bt->k_len}; }
+
+dsa::KeysDev to_dev(const dsa_kv_layout_t *ly) {
+  return dsa::KeysDev{ly->paged, ly->k_seq_start, ly->page_table, ly->page_table_stride};
+}
+
+dsa_status_t check_indexer(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i,
+                           int32_t d_i, const void *q_idx, const float *q_scale, const float *w,
+                           const void *k_idx, const float *k_scale, float scale, const float *scores,
+                           int64_t ld) {
+  dsa_status_t st = check_batch(bt);
+  if (st != DSA_OK) return st;
+  if ((st = check_layout(ly, bt, "key")) != DSA_OK) return st;
+  if (!std::isfinite(scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "indexer scale must be finite");
+  if (ld < bt->max_k_len) return fail(DSA_ERR_INVALID_ARGUMENT, "ld_scores %lld < max_k_len %d", (long long)ld, bt->max_k_len);
+  if (dt == DSA_FP8_E4M3) {
+    if (d_i != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer: d_i must be 128 (got %d)", d_i);
+    if (h_i != 32 && h_i != 64 && h_i != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer: h_i must be 32, 64 or 128 (got %d)", h_i);
+    if (bt->num_queries > 0 && (!q_scale || !k_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "FP8 indexer needs q_scale and k_scale");
+    if (!aligned(q_idx, 32) || !aligned(k_idx, 32)) return fail(DSA_ERR_INVALID_ARGUMENT, "FP8 q_idx / k_idx must be 32-byte aligned");
+  } else if (dt == DSA_F32) {
+    if (h_i < 1 || h_i > 64 || d_i < 1 || d_i > 128) return fail(DSA_ERR_UNSUPPORTED, "f32 indexer: needs 1 <= h_i <= 64, 1 <= d_i <= 128");
+    if (q_scale || k_scale) return fail(DSA_ERR_INVALID_ARGUMENT, "f32 indexer takes no scales (pass NULL)");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be DSA_F32 or DSA_FP8_E4M3");
+  }
+  if (bt->num_queries > 0 && (!q_idx || !w || !k_idx || !scores))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "indexer: q_idx, w, k_idx and scores must be non-NULL");
+  return DSA_OK;
+}
+
+dsa_status_t check_topk(const dsa_batch_t *bt, const float *scores, int64_t ld, int32_t k, const int32_t *indices) {
+  dsa_status_t st = check_batch(bt);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "top-k: k must be in [1, 65536] (got %d)", k);
+  if (ld < bt->max_k_len) return fail(DSA_ERR_INVALID_ARGUMENT, "ld_scores %lld < max_k_len %d", (long long)ld, bt->max_k_len);
+  if (bt->num_queries > 0) {
+    if (!scores || !indices) return fail(DSA_ERR_INVALID_ARGUMENT, "top-k: scores / indices is NULL");
+    if (!aligned(scores, 16) || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARGUMENT, "top-k: scores must be 16-byte aligned with ld_scores % 4 == 0");
+  }
+  return DSA_OK;
+}
+
+dsa_status_t check_mla(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t heads, int32_t d_qk,
+                       int32_t d_v, const void *q, const void *kv, const int32_t *indices, int32_t k, float sm_scale,
+                       const void *out) {
+  dsa_status_t st = check_batch(bt);
+  if (st != DSA_OK) return st;
+  if ((st = check_layout(ly, bt, "latent")) != DSA_OK) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "sparse MLA: k must be in [1, 65536] (got %d)", k);
+  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (dt == DSA_BF16) {
+    if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: d_qk must be 576 and d_v 512 (got %d, %d)", d_qk, d_v);
+    if (heads != 16 && heads != 64 && heads != 128) return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: heads must be 16, 64 or 128 (got %d)", heads);
+    if (!aligned(q, 16) || !aligned(kv, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "bf16 q / kv must be 16-byte aligned");
+  } else if (dt == DSA_F32) {
+    if (heads < 1 || d_qk < 1 || d_qk > 128 || d_v < 1 || d_v > d_qk)
+      return fail(DSA_ERR_UNSUPPORTED, "f32 sparse MLA: needs heads >= 1, 1 <= d_v <= d_qk <= 128");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be DSA_F32 or DSA_BF16");
+  }
+  if (bt->num_queries > 0 && (!q || !kv || !indices || !out))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "sparse MLA: q, kv, indices and out must be non-NULL");
+  return DSA_OK;
+}
+
+size_t mla_ws(const dsa_batch_t *bt, dsa_dtype_t dt, int32_t heads, int32_t d_v, int32_t k) {
+  if (dt != DSA_BF16) return 0;
+  return dsa::mla_bf16_workspace_bytes(bt->num_queries, heads, d_v, k);
+}
+
+// Workspace carve-up of dsa_forward: [scores][indices][mla partials], 256-byte aligned.
+struct ForwardWs {
+  int64_t ld;
+  size_t scores_off, indices_off, mla_off, total;
+};
+
+ForwardWs forward_ws(const dsa_forward_args_t *a) {
+  ForwardWs w{};
+  const size_t T = (size_t)a->batch.num_queries;
+  w.ld = a->scores ? a->ld_scores : (int64_t)round_up((size_t)a->batch.max_k_len, 4);
+  size_t off = 0;
+  w.scores_off = off;
+  if (!a->scores) off += round_up(T * (size_t)w.ld * sizeof(float), 256);
+  w.indices_off = off;
+  if (!a->indices) off += round_up(T * (size_t)a->top_k * sizeof(int32_t), 256);
+  w.mla_off = off;
+  off += round_up(mla_ws(&a->batch, a->mla_dtype, a->heads, a->d_v, a->top_k), 256);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char *dsa_status_string(dsa_status_t st) {
+  switch (st) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "unknown dsa_status_t";
+}
+
+const char *dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status_t dsa_indexer_scores(const dsa_batch_t *batch, const dsa_kv_layout_t *keys, dsa_dtype_t dtype,
+                                int32_t h_i, int32_t d_i, const void *q_idx, const float *q_scale, const float *w,
+                                const void *k_idx, const float *k_scale, float scale, float *scores,
+                                int64_t ld_scores, hipStream_t stream) {
+  dsa_status_t st = check_indexer(batch, keys, dtype, h_i, d_i, q_idx, q_scale, w, k_idx, k_scale, scale, scores,
+                                  ld_scores);
+  if (st != DSA_OK) return st;
+  if (batch->num_queries == 0) return ok();
+  const dsa::BatchDev bt = to_dev(batch);
+  const dsa::KeysDev kd = to_dev(keys);
+  hipError_t e;
+  if (dtype == DSA_FP8_E4M3)
+    e = dsa::launch_indexer_fp8(bt, kd, batch->num_queries, batch->max_k_len, h_i, (const uint8_t *)q_idx, q_scale,
+                                w, (const uint8_t *)k_idx, k_scale, scale, scores, ld_scores, stream);
+  else
+    e = dsa::launch_indexer_f32(bt, kd, batch->num_queries, batch->max_k_len, h_i, d_i, (const float *)q_idx, w,
+                                (const float *)k_idx, scale, scores, ld_scores, stream);
+  return hip_status(e, "indexer launch");
+}
+
+dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t *bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  dsa_status_t st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "top-k: k must be in [1, 65536] (got %d)", k);
+  *bytes = 0;
+  return ok();
+}
+
+dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_scores, int32_t k, int32_t *indices,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  dsa_status_t st = check_topk(batch, scores, ld_scores, k, indices);
+  if (st != DSA_OK) return st;
+  if (batch->num_queries == 0) return ok();
+  return hip_status(dsa::launch_topk(to_dev(batch), batch->num_queries, scores, ld_scores, k, indices, stream),
+                    "top-k launch");
+}
+
+dsa_status_t dsa_sparse_mla_workspace_size(const dsa_batch_t *batch, dsa_dtype_t dtype, int32_t heads, int32_t d_qk,
+                                           int32_t d_v, int32_t k, size_t *bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  dsa_status_t st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (dtype == DSA_BF16 && (d_qk != 576 || d_v != 512))
+    return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: d_qk must be 576 and d_v 512");
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "sparse MLA: k must be in [1, 65536]");
+  *bytes = mla_ws(batch, dtype, heads, d_v, k);
+  return ok();
+}
+
+dsa_status_t dsa_sparse_mla_fwd(const dsa_batch_t *batch, const dsa_kv_layout_t *kv_layout, dsa_dtype_t dtype,
+                                int32_t heads, int32_t d_qk, int32_t d_v, const void *q, const void *kv,
+                                const int32_t *indices, int32_t k, float sm_scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st = check_mla(batch, kv_layout, dtype, heads, d_qk, d_v, q, kv, indices, k, sm_scale, out);
+  if (st != DSA_OK) return st;
+  const size_t need = mla_ws(batch, dtype, heads, d_v, k);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "sparse MLA needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  if (need && !aligned(workspace, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (batch->num_queries == 0) return ok();
+  const dsa::BatchDev bt = to_dev(batch);
+  const dsa::KeysDev kd = to_dev(kv_layout);
+  hipError_t e;
+  if (dtype == DSA_BF16)
+    e = dsa::launch_mla_bf16(bt, kd, batch->num_queries, heads, q, kv, indices, k, sm_scale, out, lse, workspace,
+                             stream);
+  else
+    e = dsa::launch_mla_f32(bt, kd, batch->num_queries, heads, d_qk, d_v, (const float *)q, (const float *)kv,
+                            indices, k, sm_scale, (float *)out, lse, stream);
+  return hip_status(e, "sparse MLA launch");
+}
+
+dsa_status_t dsa_forward_workspace_size(const dsa_forward_args_t *a, size_t *bytes) {
+  if (!a || !bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "args / bytes is NULL");
+  dsa_status_t st = check_batch(&a->batch);
+  if (st != DSA_OK) return st;
+  if (a->top_k < 1 || a->top_k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "top_k must be in [1, 65536]");
+  *bytes = forward_ws(a).total;
+  return ok();
+}
+
+dsa_status_t dsa_forward(const dsa_forward_args_t *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  const ForwardWs ws = forward_ws(a);
+  const float *scores_chk = a->scores ? a->scores : (const float *)1;  // checked below once carved
+  dsa_status_t st = check_indexer(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w,
+                                  a->k_idx, a->k_scale, a->index_scale, scores_chk, ws.ld);
+  if (st != DSA_OK) return st;
+  if (a->scores && (!aligned(a->scores, 16) || ws.ld % 4 != 0))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "scores must be 16-byte aligned with ld_scores % 4 == 0");
+  if (a->top_k < 1 || a->top_k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "top_k must be in [1, 65536]");
+  st = check_mla(&a->batch, &a->layout, a->mla_dtype, a->heads, a->d_qk, a->d_v, a->q, a->kv, (const int32_t *)1,
+                 a->top_k, a->sm_scale, a->out);
+  if (st != DSA_OK) return st;
+  if (workspace_bytes < ws.total || (ws.total && !workspace))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_forward needs %zu workspace bytes, got %zu", ws.total,
+                workspace_bytes);
+  if (ws.total && !aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (a->batch.num_queries == 0) return ok();
+  uint8_t *base = (uint8_t *)workspace;
+  float *scores = a->scores ? a->scores : (float *)(base + ws.scores_off);
+  int32_t *indices = a->indices ? a->indices : (int32_t *)(base + ws.indices_off);
+  void *mla_ws_ptr = base ? base + ws.mla_off : nullptr;
+  const size_t mla_bytes = ws.total - ws.mla_off;
+
+  st = dsa_indexer_scores(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w, a->k_idx,
+                          a->k_scale, a->index_scale, scores, ws.ld, stream);
+  if (st != DSA_OK) return st;
+  st = dsa_topk(&a->batch, scores, ws.ld, a->top_k, indices, nullptr, 0, stream);
+  if (st != DSA_OK) return st;
+  return dsa_sparse_mla_fwd(&a->batch, &a->layout, a->mla_dtype, a->heads, a->d_qk, a->d_v, a->q, a->kv, indices,
+                            a->top_k, a->sm_scale, a->out, a->lse, mla_ws_ptr, mla_bytes, stream);
+}
+
+}  // extern "C"

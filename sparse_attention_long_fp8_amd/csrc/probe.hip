@@ -1,0 +1,66 @@
+// Test-only probes of gfx950 instruction semantics the libdsa kernels rely
+// on: FP8 and bf16 MFMA operand / accumulator lane layouts (and with them the
+// FP8 E4M3 interpretation of bytes) and the lane mapping of the LDS transpose
+// read.  One wave each, fully in bounds; built into libdsa_probe.so, which
+// only the test-suite loads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// a, b: [64 lanes][32 bytes] operand registers as each lane holds them;
+// d: [64 lanes][16] accumulator registers after one MFMA from zero.
+__global__ void probe_fp8_32x32x64_kernel(const v8i *a, const v8i *b, v16f *d) {
+  const int l = threadIdx.x;
+  v16f acc = {};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], acc, 0, 0, 0, 127, 0, 127);
+  d[l] = acc;
+}
+
+// a, b: [64][8] bf16; d: [64][4]
+__global__ void probe_bf16_16x16x32_kernel(const v8bf *a, const v8bf *b, v4f *d) {
+  const int l = threadIdx.x;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[l], b[l], acc, 0, 0, 0);
+  d[l] = acc;
+}
+
+// src: 4096 16-bit words copied into LDS; off: per-lane byte offset (8-byte
+// aligned, < 8192 - 8, checked on the host); dst: [64][4] words read back.
+__global__ void probe_tr16_kernel(const short *src, const int *off, v4s *dst) {
+  __shared__ short lds[4096];
+  for (int i = threadIdx.x; i < 4096; i += 64) lds[i] = src[i];
+  __syncthreads();
+  const int o = off[threadIdx.x];
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  dst[threadIdx.x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((char *)lds + o));
+}
+
+extern "C" {
+
+int dsa_probe_fp8_32x32x64(const void *a, const void *b, float *d, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_fp8_32x32x64_kernel, dim3(1), dim3(64), 0, stream, (const v8i *)a,
+                     (const v8i *)b, (v16f *)d);
+  return (int)hipGetLastError();
+}
+
+int dsa_probe_bf16_16x16x32(const void *a, const void *b, float *d, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_bf16_16x16x32_kernel, dim3(1), dim3(64), 0, stream, (const v8bf *)a,
+                     (const v8bf *)b, (v4f *)d);
+  return (int)hipGetLastError();
+}
+
+int dsa_probe_tr16(const void *src, const int *off_host, const int *off_dev, void *dst,
+                   hipStream_t stream) {
+  for (int i = 0; i < 64; ++i)
+    if (off_host[i] < 0 || off_host[i] > 8192 - 8 || (off_host[i] & 7)) return -1;
+  hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, stream, (const short *)src, off_dev,
+                     (v4s *)dst);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

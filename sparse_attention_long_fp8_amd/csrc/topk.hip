@@ -1,0 +1,287 @@
+// Per-row causal top-k (gfx950).
+//
+// For query row t with n_t candidates, writes the positions of the
+// m = min(k, n_t) largest scores in ascending order, then -1 padding
+// ("DeepSeek Sparse Attention DSA Architecture Guide", "Stage 2: Fine-Grained
+// Token Selection", TopK equation; its implementation section keeps
+// k = min(top_k, seq_len) and re-sorts the chosen positions into temporal
+// order).  Ties go to the lowest position, so the result is unique and the
+// kernel is deterministic.
+//
+// One 1024-thread workgroup owns a row and keeps it in LDS when it fits
+// (up to 32768 scores).  Selection is exact:
+//   1. min / max of the row (while caching it);
+//   2. histogram of a monotone linear binning of the values into 2048 bins
+//      (spreads typical score distributions evenly, so LDS atomics rarely
+//      collide); a wave-wide scan from the top finds the bin b* holding the
+//      k-th largest score;
+//   3. exact radix select (11/11/10-bit digits of an order-preserving uint32
+//      key) over the elements of bin b* only -- compacted into an LDS list
+//      when there are at most 1024 of them -- yields the threshold key tau
+//      and how many elements equal to tau are kept;
+//   4. one ordered pass writes key > tau, plus the first `need_eq` elements
+//      equal to tau, at positions given by wave ballots and a block scan of
+//      per-wave counts: the output comes out ascending.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+constexpr int kTkThreads = 1024;
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkCache = 32768;  // scores kept in LDS (128 KiB)
+constexpr int kTkBins = 2048;
+constexpr int kTkCand = 1024;
+
+struct TopkLds {
+  float cache[kTkCache];
+  uint32_t hist[kTkBins];
+  int32_t cand[kTkCand];
+  uint32_t red_lo[kTkWaves];
+  uint32_t red_hi[kTkWaves];
+  int32_t cnt[2][2][kTkWaves];
+  int32_t scan_bin;
+  int32_t scan_above;
+  int32_t cand_count;
+};
+
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Wave 0 only.  Finds the bin d such that the count strictly above d is
+// < need and the count from d upward is >= need.  Lane l sums the l-th
+// group of nbins/64 bins counted from the top; an inclusive lane scan picks
+// the group, whose lane then walks its bins.
+__device__ void scan_from_top(const uint32_t *hist, int nbins, int need, int32_t *out_bin,
+                              int32_t *out_above) {
+  const int lane = lane_id();
+  const int c = nbins / 64;
+  const int hi = nbins - lane * c;
+  int s = 0;
+  for (int j = 1; j <= c; ++j) s += (int)hist[hi - j];
+  int incl = s;
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const uint64_t hit = __ballot(incl >= need);
+  if (hit == 0) {  // only with NaN scores (a precondition violation)
+    if (lane == 0) { *out_bin = 0; *out_above = 0; }
+    return;
+  }
+  const int first = __ffsll((unsigned long long)hit) - 1;
+  if (lane == first) {
+    int run = incl - s;
+    int bin = hi - c, above = run;
+    for (int j = 1; j <= c; ++j) {
+      int h = (int)hist[hi - j];
+      if (run + h >= need) { bin = hi - j; above = run; break; }
+      run += h;
+    }
+    *out_bin = bin;
+    *out_above = above;
+  }
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
+                                                         const float *__restrict__ scores,
+                                                         int64_t ld, int k,
+                                                         int32_t *__restrict__ indices) {
+  __shared__ TopkLds sh;
+  const int t = blockIdx.x;
+  const int b = seq_of_row(bt, t);
+  const int n = candidates_of_row(bt, b, t);
+  int32_t *out = indices + (int64_t)t * k;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  if (n <= k) {  // every candidate is kept
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float *row = scores + (int64_t)t * ld;
+  const bool cached = n <= kTkCache;
+  auto load4 = [&](int i) -> float4 {
+    return cached ? *(const float4 *)(&sh.cache[i]) : *(const float4 *)(row + i);
+  };
+
+  // ---- 1. cache the row, min / max key ----
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
+    float4 v = *(const float4 *)(row + i);
+    if (cached) *(float4 *)(&sh.cache[i]) = v;
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + j < n) {
+        uint32_t key = float_key(f[j]);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { sh.red_lo[wave] = kmin; sh.red_hi[wave] = kmax; }
+  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  kmin = sh.red_lo[0];
+  kmax = sh.red_hi[0];
+  for (int w2 = 1; w2 < kTkWaves; ++w2) {
+    kmin = min(kmin, sh.red_lo[w2]);
+    kmax = max(kmax, sh.red_hi[w2]);
+  }
+  const float fmin = key_to_float(kmin);
+  const float fmax = key_to_float(kmax);
+  float inv = (float)kTkBins / (fmax - fmin);
+  if (!(fmax > fmin) || !(inv < 3.0e38f)) inv = 0.f;  // degenerate range: one bin
+  auto bin_of = [&](float f) -> int {
+    return (int)fminf(fmaxf((f - fmin) * inv, 0.f), (float)(kTkBins - 1));
+  };
+
+  // ---- 2. histogram, threshold bin ----
+  for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
+    float4 v = load4(i);
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + j < n) atomicAdd(&sh.hist[bin_of(f[j])], 1u);
+  }
+  __syncthreads();
+  if (wave == 0) scan_from_top(sh.hist, kTkBins, k, &sh.scan_bin, &sh.scan_above);
+  __syncthreads();
+  const int bstar = sh.scan_bin;
+  int need = k - sh.scan_above;
+  const int bcount = (int)sh.hist[bstar];
+  const bool use_list = bcount <= kTkCand;
+  if (tid == 0) sh.cand_count = 0;
+  __syncthreads();
+
+  // ---- 3. exact threshold inside bin b* ----
+  if (use_list) {
+    for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
+      float4 v = load4(i);
+      const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j < n && bin_of(f[j]) == bstar) {
+          int slot = atomicAdd(&sh.cand_count, 1);
+          if (slot < kTkCand) sh.cand[slot] = i + j;
+        }
+    }
+    __syncthreads();
+  }
+  const int ncand = min(bcount, kTkCand);
+  uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < nb; i += kTkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    if (use_list) {
+      for (int c = tid; c < ncand; c += kTkThreads) {
+        const int pos = sh.cand[c];
+        const uint32_t key = float_key(cached ? sh.cache[pos] : row[pos]);
+        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+      }
+    } else {
+      for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
+        float4 v = load4(i);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t key = float_key(f[j]);
+          if (i + j < n && bin_of(f[j]) == bstar && (key & pmask) == prefix)
+            atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) scan_from_top(sh.hist, nb, need, &sh.scan_bin, &sh.scan_above);
+    __syncthreads();
+    need -= sh.scan_above;
+    prefix |= (uint32_t)sh.scan_bin << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;
+  const int need_eq = need;
+
+  // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
+  int gt_run = 0, eq_run = 0;
+  int it = 0;
+  for (int base = 0; base < n; base += 4 * kTkThreads, ++it) {
+    const int i = base + 4 * tid;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n) v = load4(i);
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    bool gt[4], eq[4];
+    int g_lane = 0, e_lane = 0, g_tot = 0, e_tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t key = float_key(f[j]);
+      const bool valid = i + j < n;
+      gt[j] = valid && key > tau;
+      eq[j] = valid && key == tau;
+      const uint64_t bg = __ballot(gt[j]);
+      const uint64_t be = __ballot(eq[j]);
+      g_lane += lanes_below(bg);
+      e_lane += lanes_below(be);
+      g_tot += __popcll(bg);
+      e_tot += __popcll(be);
+    }
+    const int slot = it & 1;
+    if (lane == 0) { sh.cnt[slot][0][wave] = g_tot; sh.cnt[slot][1][wave] = e_tot; }
+    __syncthreads();
+    int g_wave = 0, e_wave = 0, g_blk = 0, e_blk = 0;
+    for (int w2 = 0; w2 < kTkWaves; ++w2) {
+      const int gv = sh.cnt[slot][0][w2];
+      const int ev = sh.cnt[slot][1][w2];
+      if (w2 < wave) { g_wave += gv; e_wave += ev; }
+      g_blk += gv;
+      e_blk += ev;
+    }
+    int g_before = gt_run + g_wave + g_lane;
+    int e_before = eq_run + e_wave + e_lane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (gt[j]) {
+        const int pos = g_before + min(e_before, need_eq);
+        if (pos < k) out[pos] = i + j;
+        ++g_before;
+      } else if (eq[j]) {
+        if (e_before < need_eq) {
+          const int pos = g_before + e_before;
+          if (pos < k) out[pos] = i + j;
+        }
+        ++e_before;
+      }
+    }
+    gt_run += g_blk;
+    eq_run += e_blk;
+  }
+  const int total = gt_run + min(eq_run, need_eq);
+  for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
+}
+
+hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
+                       int k, int32_t *indices, hipStream_t stream) {
+  if (num_queries == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld,
+                     k, indices);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

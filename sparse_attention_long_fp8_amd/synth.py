@@ -48,7 +48,7 @@ T_CTX, T_QI, T_W, T_KI, T_Q, T_KV, T_STRUCT, T_PERM = range(8)
 class Workload:
     name: str
     seed: int
-    kind: str                 # "prefill" or "decode"
+    kind: str                 # "prefill", "decode" or "chunk" (q_per_seq new queries)
     batch: int
     ctx: int                  # prefill length, or fixed decode history
     ctx_range: tuple = None   # (lo, hi) inclusive for ragged decode
@@ -63,6 +63,7 @@ class Workload:
     needles: int = 0
     drift_block: int = 0      # >0: keys carry 0.5 * per-block shared drift
     index_scale: float = 1.0  # multiplies every indexer score
+    q_per_seq: int = 0        # "chunk": queries per sequence (the last tokens of each history)
 
     @property
     def d_qk(self) -> int:
@@ -195,6 +196,8 @@ def make_layout(wl: Workload) -> Layout:
         else:
             k_len = np.array([wl.ctx] * wl.batch, dtype=np.int64)
         nq = np.ones(wl.batch, dtype=np.int64)
+        if wl.kind == "chunk":
+            nq = np.minimum(k_len, wl.q_per_seq)
     q_seq_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     k_seq_start = np.concatenate([[0], np.cumsum(k_len)]).astype(np.int64)
     lay = Layout(q_seq_start=q_seq_start, k_len=k_len.astype(np.int32),

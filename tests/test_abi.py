@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and argument validation returns the documented status
+codes before anything is launched."""
+
+import ctypes
+
+import pytest
+
+from sparse_attention_long_fp8_amd import binding as B
+
+
+def _batch(T=4, B_=1, maxq=4, maxk=8):
+    # fake, never-dereferenced device addresses: validation only reads host fields
+    return B.dsa_batch_t(B_, T, 0x1000, 0x2000, maxq, maxk)
+
+
+def _layout(rows=8):
+    return B.dsa_kv_layout_t(0, 0x3000, None, 0, 64, rows)
+
+
+def test_exports_match_header():
+    lib = B.lib()
+    names = B.header_functions()
+    assert len(names) == 10
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings():
+    assert B.dsa_abi_version() == 1
+    assert B.dsa_status_string(0) == "DSA_OK"
+    assert B.dsa_status_string(4) == "DSA_ERR_HIP"
+    assert "unknown" in B.dsa_status_string(99)
+
+
+def test_null_and_bad_arguments():
+    lib = B.lib()
+    st = lib.dsa_indexer_scores(None, None, B.DSA_F32, 4, 32, None, None, None, None, None, 1.0, None, 8, None)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+    assert "batch" in B.dsa_last_error()
+    bt, ly = _batch(), _layout()
+    # f32 indexer must not be given scales
+    st = B.dsa_indexer_scores(bt, ly, B.DSA_F32, 4, 32, 0x10, 0x20, 0x30, 0x40, 0x50, 1.0, 0x60, 8, check=False)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+    # FP8 indexer only implements d_i = 128
+    st = B.dsa_indexer_scores(bt, ly, B.DSA_FP8_E4M3, 64, 64, 0x100, 0x20, 0x30, 0x200, 0x50, 1.0, 0x60, 8,
+                              check=False)
+    assert st == B.DSA_ERR_UNSUPPORTED
+    # ld_scores shorter than the longest history
+    st = B.dsa_indexer_scores(bt, ly, B.DSA_F32, 4, 32, 0x10, None, 0x30, 0x40, None, 1.0, 0x60, 7, check=False)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+    # queries must be the last tokens of their history
+    bad = _batch(T=4, maxq=9, maxk=8)
+    st = B.dsa_topk(bad, 0x1000, 8, 4, 0x2000, check=False)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+    # k range, alignment of the score rows
+    assert B.dsa_topk(bt, 0x1000, 8, 0, 0x2000, check=False) == B.DSA_ERR_INVALID_ARGUMENT
+    assert B.dsa_topk(bt, 0x1004, 8, 4, 0x2000, check=False) == B.DSA_ERR_INVALID_ARGUMENT
+    assert B.dsa_topk(bt, 0x1000, 10, 4, 0x2000, check=False) == B.DSA_ERR_INVALID_ARGUMENT
+    # bf16 MLA only implements 576 / 512
+    st = B.dsa_sparse_mla_fwd(bt, ly, B.DSA_BF16, 128, 128, 128, 0x100, 0x200, 0x300, 4, 0.1, 0x400, None,
+                              check=False)
+    assert st == B.DSA_ERR_UNSUPPORTED
+    st = B.dsa_sparse_mla_fwd(bt, ly, B.DSA_BF16, 96, 576, 512, 0x100, 0x200, 0x300, 4, 0.1, 0x400, None,
+                              check=False)
+    assert st == B.DSA_ERR_UNSUPPORTED
+    # non-finite softmax scale
+    st = B.dsa_sparse_mla_fwd(bt, ly, B.DSA_F32, 4, 80, 64, 0x100, 0x200, 0x300, 4, float("inf"), 0x400, None,
+                              check=False)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+    # paged layout: only 64-token pages, table must cover max_k_len
+    paged = B.dsa_kv_layout_t(1, None, 0x5000, 1, 32, 10)
+    st = B.dsa_sparse_mla_fwd(bt, paged, B.DSA_F32, 4, 80, 64, 0x100, 0x200, 0x300, 4, 0.1, 0x400, None,
+                              check=False)
+    assert st == B.DSA_ERR_UNSUPPORTED
+    paged = B.dsa_kv_layout_t(1, None, 0x5000, 0, 64, 10)
+    st = B.dsa_sparse_mla_fwd(bt, paged, B.DSA_F32, 4, 80, 64, 0x100, 0x200, 0x300, 4, 0.1, 0x400, None,
+                              check=False)
+    assert st == B.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_and_too_small():
+    # decode-sized batch: the split MLA needs partials; prefill-sized: none
+    dec = B.dsa_batch_t(32, 32, 0x1000, 0x2000, 1, 32768)
+    ws = B.dsa_sparse_mla_workspace_size(dec, B.DSA_BF16, 128, 576, 512, 2048)
+    assert ws > 0 and ws % 4 == 0
+    pre = B.dsa_batch_t(1, 16384, 0x1000, 0x2000, 16384, 16384)
+    assert B.dsa_sparse_mla_workspace_size(pre, B.DSA_BF16, 128, 576, 512, 2048) == 0
+    assert B.dsa_topk_workspace_size(pre, 2048) == 0
+    st = B.dsa_sparse_mla_fwd(dec, _layout(1 << 20), B.DSA_BF16, 128, 576, 512, 0x100, 0x200, 0x300, 2048, 0.04,
+                              0x400, None, None, ws - 1, check=False)
+    assert st == B.DSA_ERR_WORKSPACE_TOO_SMALL
+    args = B.forward_args(dec, _layout(1 << 20), index_dtype=B.DSA_FP8_E4M3, h_i=64, d_i=128, q_idx=0x1000,
+                          q_scale=0x2000, w=0x3000, k_idx=0x4000, k_scale=0x5000, index_scale=1.0, top_k=2048,
+                          mla_dtype=B.DSA_BF16, heads=128, d_qk=576, d_v=512, q=0x6000, kv=0x7000,
+                          sm_scale=0.04, out=0x8000)
+    need = B.dsa_forward_workspace_size(args)
+    # scores [32, 32768] fp32 + indices [32, 2048] int32 + MLA partials, each 256-byte aligned
+    assert need >= 32 * 32768 * 4 + 32 * 2048 * 4 + ws
+    assert B.dsa_forward(args, 0x100000, need - 1, check=False) == B.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert B.dsa_forward(args, 0x100010, need, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # misaligned
+
+
+def test_empty_batch_launches_nothing():
+    empty = B.dsa_batch_t(1, 0, None, None, 0, 0)
+    ly = _layout(1)
+    assert B.dsa_topk(empty, None, 0, 8, None, check=False) == B.DSA_OK
+    assert B.dsa_indexer_scores(empty, ly, B.DSA_F32, 4, 32, None, None, None, None, None, 1.0, None, 0,
+                                check=False) == B.DSA_OK
+    assert B.dsa_sparse_mla_fwd(empty, ly, B.DSA_F32, 4, 80, 64, None, None, None, 8, 0.1, None, None,
+                                check=False) == B.DSA_OK
+
+
+def test_struct_layouts_match_c():
+    # the ctypes mirrors must have the C sizes (x86-64 SysV)
+    assert ctypes.sizeof(B.dsa_batch_t) == 32
+    assert ctypes.sizeof(B.dsa_kv_layout_t) == 40
+    assert B.dsa_forward_args_t.ld_scores.offset % 8 == 0
+
+
+def test_struct_offsets_match_a_c_compiler(tmp_path):
+    """Offsets of the ctypes mirrors equal what gcc computes from the header."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    fields = [f for f, _ in B.dsa_forward_args_t._fields_]
+    src = tmp_path / "offs.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "libdsa.h"\nint main(void){\n'
+        '  printf("%zu %zu %zu\\n", sizeof(dsa_batch_t), sizeof(dsa_kv_layout_t), sizeof(dsa_forward_args_t));\n'
+        + "".join('  printf("%%zu\\n", offsetof(dsa_forward_args_t, %s));\n' % f for f in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "offs"
+    inc = B.HEADER.rsplit("/", 1)[0]
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + inc, str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    sizes = [int(x) for x in out[:3]]
+    assert sizes == [ctypes.sizeof(B.dsa_batch_t), ctypes.sizeof(B.dsa_kv_layout_t),
+                     ctypes.sizeof(B.dsa_forward_args_t)]
+    assert [int(x) for x in out[3:]] == [getattr(B.dsa_forward_args_t, f).offset for f in fields]

@@ -1,0 +1,95 @@
+"""Parity of the HIP path with the CPU oracle on seeded inputs, stage by stage
+and end to end, through the C ABI.  Sizes here let the oracle check every
+row while spanning several tiles and a ragged tail; full workload sizes are
+in test_gpu_full.py."""
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_long_fp8_amd import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+SMALL = {
+    # the tiny fp32 workload, exactly as measured (L=512, H_I=4 x 32, k=64, 4 heads 80/64)
+    "tiny_prefill": synth.WORKLOADS["tiny_prefill"],
+    # FP8 / bf16 shapes of the large workloads at a size the oracle checks in full:
+    # 300 rows -> several 32-key tiles and a ragged tail; k=64 < n for most rows
+    "prefill_300": W("prefill_300", 10, "prefill", 1, 300, top_k=64),
+    # ragged decode, contiguous cache, k=256
+    "decode_ragged": W("decode_ragged", 11, "decode", 5, 0, ctx_range=(100, 3000), top_k=256),
+    # ragged decode from a permuted 64-token page pool with poisoned tails
+    "decode_paged": W("decode_paged", 12, "decode", 4, 0, ctx_range=(70, 2000), paged=True, top_k=128),
+    # chunked prefill: 40 new queries after a cached prefix, two sequences
+    "chunk_2x40": W("chunk_2x40", 13, "chunk", 2, 0, ctx_range=(200, 700), q_per_seq=40, top_k=96),
+    # single-head page form: H_I = 32 (smallest FP8 head count), 1/sqrt(d_I) scale, 16 MLA heads
+    "prefill_h32": W("prefill_h32", 14, "prefill", 1, 200, h_i=32, top_k=50, heads=16,
+                     index_scale=1.0 / np.sqrt(128)),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def case(request, gpu):
+    print("\n[case] %s" % request.param, flush=True)
+    return H.GpuCase(SMALL[request.param], gpu)
+
+
+def test_stages(case):
+    rows = list(range(case.T))
+    scores = case.indexer()
+    refs = H.check_indexer(case, scores, rows)
+    idx = case.topk(scores)
+    H.check_topk_exact(case, scores, idx, rows)
+    H.check_topk_end_to_end(case, refs, idx, rows)
+    out, lse = case.mla(idx)
+    worst = H.check_mla(case, idx, out, lse, rows)
+    print("[%s] worst attention error %.3g" % (case.wl.name, worst))
+
+
+def test_forward_equals_stages_and_is_deterministic(case):
+    s1, i1, o1, l1 = case.forward()
+    s2, i2, o2, l2 = case.forward()
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1,
+                                               o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2)
+    scores = case.indexer()
+    n_of = [r[2] for r in case.rows]
+    for t in range(case.T):
+        assert torch.equal(scores[t, :n_of[t]], s1[t, :n_of[t]])
+    idx = case.topk(scores)
+    assert torch.equal(idx, i1)
+    out, lse = case.mla(idx)
+    assert torch.equal(out.float(), o1.float()) and torch.equal(lse, l1)
+    # the internal-workspace variant gives the same result
+    _, _, o3, l3 = case.forward(keep=False)
+    assert torch.equal(o3.float(), o1.float()) and torch.equal(l3, l1)
+
+
+def test_paged_equals_contiguous(gpu):
+    wl = SMALL["decode_paged"]
+    paged = H.GpuCase(wl, gpu)
+    flat = H.GpuCase(wl, gpu, force_contiguous=True)
+    sp, ip, op, lp = paged.forward()
+    sf, if_, of, lf = flat.forward()
+    for t in range(paged.T):
+        n = paged.rows[t][2]
+        assert torch.equal(sp[t, :n], sf[t, :n])
+    assert torch.equal(ip, if_)
+    assert torch.equal(op.float(), of.float()) and torch.equal(lp, lf)
+
+
+def test_k_at_least_context_is_dense_attention(gpu):
+    """With k >= every n_t the selection is all of 0..t and attention is dense causal."""
+    from oracle import dsa_oracle as O
+    wl = W("dense_check", 15, "prefill", 1, 96, top_k=128)
+    c = H.GpuCase(wl, gpu)
+    _, idx, out, lse = c.forward()
+    i = idx.cpu().numpy()
+    for t in range(c.T):
+        assert i[t, :t + 1].tolist() == list(range(t + 1)) and (i[t, t + 1:] == -1).all()
+    o_d, lse_d = O.dense_causal_mla(c.q_hat[:24], c.kv_hat[:24], wl.d_v, wl.sm_scale)
+    o = out.float().cpu().numpy()[:24]
+    assert np.abs(o - o_d).max() / np.abs(o_d).max() <= H.ATTN_TOL_BF16
+    assert np.abs(lse.cpu().numpy()[:24] - lse_d).max() <= H.LSE_TOL
