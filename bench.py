@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA hot path (lightning indexer -> top-k -> sparse MLA)
+on one MI355X, through the libdsa C ABI.
+
+A step is one pass of the whole path over the workload's batch: the three
+stages are launched back to back on torch's current stream (exactly what
+dsa_forward enqueues), with HIP events between them so that every stage's
+average duration is measured live over the timed region.  Inputs are
+resident in HBM before timing starts; for the decode workloads several
+copies of every input are rotated so that no step finds its inputs in the
+256 MB Infinity Cache left there by the previous one.
+
+Prints one JSON line.  Default workload: 32 single-token decodes over 32768
+cached tokens (FP8 indexer 64x128, k = 2048, 128-head 576/512 bf16 MLA).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query-tokens/sec through indexer+top-k+sparse MLA; decode µs/step; % roofline"
+HBM_PEAK = 8.0e12      # bytes/s, MI355X HBM3E
+FP8_PEAK = 5.0e15      # dense FP8 MFMA flop/s
+BF16_PEAK = 2.5e15     # dense BF16 MFMA flop/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 200 decode, 10 prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: 20 decode, 3 prefill)")
+    ap.add_argument("--workload", default="decode_32k",
+                    help="decode_32k | prefill_16k | prefill_64k | paged_decode | tiny_prefill")
+    ap.add_argument("--copies", type=int, default=None, help="input copies rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU oracle work for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run the plain copy kernel on MIB mebibytes (counter calibration) and exit")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic work of each stage (what the method must move / compute)
+# --------------------------------------------------------------------------
+def stage_work(wl, lay):
+    rows_n = []
+    for b in range(wl.batch):
+        nq = int(lay.q_seq_start[b + 1] - lay.q_seq_start[b])
+        kl = int(lay.k_len[b])
+        rows_n.extend(range(kl - nq + 1, kl + 1))
+    n = np.array(rows_n, dtype=np.float64)
+    T = len(rows_n)
+    m = np.minimum(n, wl.top_k)
+    pairs, sel = n.sum(), m.sum()
+    if wl.fp8:
+        idx_bytes = pairs * (wl.d_i + 4 + 4) + T * (wl.h_i * wl.d_i + 4 + 4 * wl.h_i)
+        el = 2
+    else:
+        idx_bytes = pairs * (4 * wl.d_i + 4) + T * (4 * wl.h_i * wl.d_i + 4 * wl.h_i)
+        el = 4
+    return {
+        "indexer": {"bytes": idx_bytes, "flops": pairs * wl.h_i * wl.d_i * 2,
+                    "peak_flops": FP8_PEAK if wl.fp8 else 157.3e12},
+        "topk": {"bytes": pairs * 4 + T * wl.top_k * 4, "flops": 0.0, "peak_flops": None},
+        "mla": {"bytes": sel * wl.d_qk * el + T * wl.heads * (wl.d_qk + wl.d_v) * el + T * wl.heads * 4
+                + T * wl.top_k * 4,
+                "flops": sel * wl.heads * (wl.d_qk + wl.d_v) * 2,
+                "peak_flops": BF16_PEAK if wl.fp8 else 157.3e12},
+        "pairs": pairs, "selected": sel, "queries": T,
+    }
+
+
+KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
+KERNEL_NAMES = {"indexer": "indexer_fp8_kernel", "topk": "topk_kernel", "mla": "mla_bf16_kernel"}
+
+
+def source_hash(stage):
+    path = os.path.join(ROOT, "sparse_attention_long_fp8_amd", "csrc", KERNEL_SOURCES[stage])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_of(stage, workload):
+    """HBM bytes per launch from committed counter summaries, if they were
+    taken on the current kernel source; None otherwise."""
+    path = os.path.join(PROFILES, "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(stage)
+    if not rec or rec.get("source_sha256_16") != source_hash(stage):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# --------------------------------------------------------------------------
+def cpu_baseline(wl, synth_obj, budget_s):
+    from oracle import dsa_oracle as O
+    lay = synth_obj.layout
+    rows = O.query_rows(lay.q_seq_start, lay.k_len)
+    order = list(range(len(rows)))
+    if wl.kind == "prefill":  # spread the sample over the causal range
+        rng = np.random.default_rng(0)
+        order = list(rng.permutation(len(rows)))
+    done, cost_done = 0, 0.0
+    t_start = time.perf_counter()
+    elapsed = 0.0
+    for t in order:
+        b, p, n = rows[t]
+        base = int(lay.k_seq_start[b])
+        qi, qs = synth_obj.qi(t, t + 1)
+        ki, ks = synth_obj.ki(base, base + n)
+        q = synth_obj.q(t, t + 1)
+        kv = synth_obj.kv(base, base + n)
+        w = synth_obj.w(t, t + 1)[0]
+        t0 = time.perf_counter()
+        if wl.fp8:
+            qi_h, ki_h = O.dequant_e4m3(qi, qs)[0], O.dequant_e4m3(ki, ks)
+            q_h, kv_h = O.decode_bf16(q)[0], O.decode_bf16(kv)
+        else:
+            qi_h, ki_h, q_h, kv_h = qi[0].astype(float), ki.astype(float), q[0].astype(float), kv.astype(float)
+        O.forward_row(qi_h, w, ki_h, q_h, kv_h, n, wl.top_k, wl.index_scale, wl.d_v, wl.sm_scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(i["num_threads"] for i in blas) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"value": done / elapsed, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d of %d query rows of %s (%s), each the full path: indexer over all n_t keys, "
+                      "top-k, sparse MLA; float64 numpy; %.1f s of oracle time" % (
+                          done, len(rows), wl.name, "first rows" if wl.kind != "prefill" else "random rows",
+                          elapsed)}
+
+
+# --------------------------------------------------------------------------
+def calibrate_copy(mib):
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_long_fp8_amd", "libdsa_probe.so"))
+    lib.dsa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        assert lib.dsa_probe_copy(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU form in this library "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    from sparse_attention_long_fp8_amd import binding as B
+    from sparse_attention_long_fp8_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    decode = wl.kind != "prefill"
+    steps = args.steps if args.steps is not None else (200 if decode else 10)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    copies = args.copies if args.copies is not None else (4 if decode else 1)
+    dev = torch.device("cuda:0")
+    B.lib()  # fail loudly now if the library is missing
+
+    s = synth.Synth(wl)
+    lay = s.layout
+    T, N = lay.num_queries, int(lay.k_seq_start[-1])
+    print("[bench] %s: generating inputs (T=%d, keys=%d)" % (wl.name, T, N), file=sys.stderr, flush=True)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def upload_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q_seq_start, k_len = i32(lay.q_seq_start), i32(lay.k_len)
+    k_seq_start = torch.from_numpy(lay.k_seq_start[:-1].astype(np.int64)).to(dev)
+    batch = B.make_batch(q_seq_start, k_len, wl.batch, T, lay.max_q_per_seq, lay.max_k_len)
+    ld = (lay.max_k_len + 3) // 4 * 4
+    dt_q = torch.bfloat16 if wl.fp8 else torch.float32
+    # inputs, generated in slabs straight into device tensors
+    qi = torch.empty((T, wl.h_i, wl.d_i), dtype=torch.uint8 if wl.fp8 else torch.float32, device=dev)
+    qs = torch.empty(T, dtype=torch.float32, device=dev) if wl.fp8 else None
+    w = torch.empty((T, wl.h_i), dtype=torch.float32, device=dev)
+    q = torch.empty((T, wl.heads, wl.d_qk), dtype=dt_q, device=dev)
+    slab = 2048
+    for r0 in range(0, T, slab):
+        r1 = min(T, r0 + slab)
+        c, sc = s.qi(r0, r1)
+        qi[r0:r1] = torch.from_numpy(c).to(dev)
+        if wl.fp8:
+            qs[r0:r1] = torch.from_numpy(sc).to(dev)
+        w[r0:r1] = torch.from_numpy(s.w(r0, r1)).to(dev)
+        qq = s.q(r0, r1)
+        q[r0:r1] = upload_bf16(qq) if wl.fp8 else torch.from_numpy(qq).to(dev)
+    if wl.paged:
+        ki_pool, ks_pool, kv_pool = s.paged_pools()
+        ki = torch.from_numpy(ki_pool).to(dev)
+        ks = torch.from_numpy(ks_pool).to(dev)
+        kv = upload_bf16(kv_pool)
+        page_table = i32(lay.page_table)
+        layout = B.make_paged_layout(page_table, lay.page_table.shape[1], lay.num_pages)
+    else:
+        ki = torch.empty((N, wl.d_i), dtype=torch.uint8 if wl.fp8 else torch.float32, device=dev)
+        ks = torch.empty(N, dtype=torch.float32, device=dev) if wl.fp8 else None
+        kv = torch.empty((N, wl.d_qk), dtype=dt_q, device=dev)
+        for g0 in range(0, N, 65536):
+            g1 = min(N, g0 + 65536)
+            c, sc = s.ki(g0, g1)
+            ki[g0:g1] = torch.from_numpy(c).to(dev)
+            if wl.fp8:
+                ks[g0:g1] = torch.from_numpy(sc).to(dev)
+            kk = s.kv(g0, g1)
+            kv[g0:g1] = upload_bf16(kk) if wl.fp8 else torch.from_numpy(kk).to(dev)
+        layout = B.make_contiguous_layout(k_seq_start, N)
+    sets = [(qi, qs, w, q, ki, ks, kv)]
+    for _ in range(copies - 1):
+        sets.append(tuple(None if x is None else x.clone() for x in sets[0]))
+    index_dtype = B.DSA_FP8_E4M3 if wl.fp8 else B.DSA_F32
+    mla_dtype = B.DSA_BF16 if wl.fp8 else B.DSA_F32
+    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, wl.heads, wl.d_v), dtype=dt_q, device=dev)
+    lse = torch.empty((T, wl.heads), dtype=torch.float32, device=dev)
+    ws_bytes = B.dsa_sparse_mla_workspace_size(batch, mla_dtype, wl.heads, wl.d_qk, wl.d_v, wl.top_k)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        qi_, qs_, w_, q_, ki_, ks_, kv_ = sets[i % copies]
+        if ev:
+            ev[0].record(stream)
+        B.dsa_indexer_scores(batch, layout, index_dtype, wl.h_i, wl.d_i, qi_, qs_, w_, ki_, ks_, wl.index_scale,
+                             scores, ld, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        B.dsa_topk(batch, scores, ld, wl.top_k, idx, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        B.dsa_sparse_mla_fwd(batch, layout, mla_dtype, wl.heads, wl.d_qk, wl.d_v, q_, kv_, idx, wl.top_k,
+                             wl.sm_scale, out, lse, ws, ws_bytes, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    print("[bench] warmup %d, timed %d steps, %d input copies" % (warmup, steps, copies), file=sys.stderr,
+          flush=True)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_step = total_ms / steps
+    stage_ms = {
+        "indexer": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+        "mla": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
+    }
+    work = stage_work(wl, lay)
+    rooflines = {}
+    for st_name in ("indexer", "topk", "mla"):
+        t_s = stage_ms[st_name] / 1e3
+        wk = work[st_name]
+        if decode or wk["peak_flops"] is None:
+            ach = wk["bytes"] / t_s
+            rooflines[st_name] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                  "frac": ach / HBM_PEAK}
+        else:
+            ach = wk["flops"] / t_s
+            rooflines[st_name] = {"bound": "mfma", "achieved": ach / 1e12, "peak": wk["peak_flops"] / 1e12,
+                                  "unit": "TFLOP/s", "frac": ach / wk["peak_flops"]}
+        tr = traffic_of(st_name, wl.name)
+        rooflines[st_name]["traffic"] = tr
+        rooflines[st_name]["kernel"] = KERNEL_NAMES[st_name]
+        rooflines[st_name]["us"] = stage_ms[st_name] * 1e3
+    dominant = max(stage_ms, key=stage_ms.get)
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_step / 1e3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3+bf16" if wl.fp8 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "queries": T, "batch": wl.batch, "kind": wl.kind,
+                   "max_ctx": lay.max_k_len, "top_k": wl.top_k, "h_i": wl.h_i, "d_i": wl.d_i,
+                   "heads": wl.heads, "d_qk": wl.d_qk, "d_v": wl.d_v, "paged": wl.paged,
+                   "input_copies": copies},
+        "decode_us_per_step": ms_step * 1e3 if decode else None,
+        "roofline": dict(rooflines[dominant]),
+        "stages": rooflines,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline (budget %.0f s)" % args.cpu_budget, file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, s, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -44,11 +44,36 @@ def _run(cmd, verbose):
         print(err)
 
 
+SCRATCH_LIMIT = 16  # bytes per lane
+
+
+def _check_no_scratch(src, verbose):
+    """Fail the build if a kernel keeps more than a few dwords in scratch
+    memory.  A spilled or dynamically indexed register array (>= 128 bytes
+    per lane here) costs far more than any of these kernels' arithmetic; a
+    few spilled loop-invariant dwords outside the hot loops do not."""
+    cmd = [HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+                              "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    fn, bad = None, []
+    for line in r.stderr.splitlines():
+        if "Function Name:" in line:
+            fn = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if n > SCRATCH_LIMIT:
+                bad.append("%s (%d bytes/lane)" % (fn, n))
+    if bad:
+        raise RuntimeError("%s: kernels spill to scratch memory: %s" % (src, ", ".join(bad)))
+
+
 def _compile(src, verbose):
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     _run([HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    if src.endswith(".hip"):
+        _check_no_scratch(src, verbose)
     return obj
 
 

@@ -40,7 +40,22 @@ __global__ void probe_tr16_kernel(const short *src, const int *off, v4s *dst) {
   dst[threadIdx.x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((char *)lds + o));
 }
 
+// Plain 16-byte-per-lane copy: the known-size reference that HBM traffic
+// counters of the other kernels are scaled by.
+__global__ void copy_kernel(const int4 *src, int4 *dst, long long n16) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n16;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 extern "C" {
+
+int dsa_probe_copy(const void *src, void *dst, long long bytes, hipStream_t stream) {
+  if (bytes % 16) return -1;
+  hipLaunchKernelGGL(copy_kernel, dim3(4096), dim3(256), 0, stream, (const int4 *)src, (int4 *)dst,
+                     bytes / 16);
+  return (int)hipGetLastError();
+}
 
 int dsa_probe_fp8_32x32x64(const void *a, const void *b, float *d, hipStream_t stream) {
   hipLaunchKernelGGL(probe_fp8_32x32x64_kernel, dim3(1), dim3(64), 0, stream, (const v8i *)a,

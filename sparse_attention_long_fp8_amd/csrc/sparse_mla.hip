@@ -87,53 +87,63 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, in
 }
 
 // --------------------------------------------------------------------------
-// bf16 path: d_qk = 576 (512 latent + 64 rotary), d_v = 512, heads = 16*NW.
+// bf16 path: d_qk = 576 (512 latent + 64 rotary), d_v = 512.
 //
-// A workgroup of NW waves takes one query row (all its heads; wave w owns
-// heads 16w..16w+15) and a contiguous range of its selected slots.  Slots
-// are processed 32 at a time.  The 32 selected 1152-byte key rows are
-// gathered straight into an LDS tile with 16-byte global->LDS loads (row
-// pitch 1168 bytes to spread LDS banks; the tile is double buffered, so the
-// next tile's loads are in flight while the current one is used).  Per wave:
-//   S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16]
-//       (16x16x32 bf16 MFMA; the query stays in registers as the B operand)
-//   online softmax per head on the accumulators (exp2 domain);
-//   O[16 heads x 512] += P[16 x 32] . V[32 x 512]
-// The S^T accumulator of lane (g, head) holds tokens 4g+i of each 16-token
-// half, which is exactly the A-operand slot set of the PV product once the
-// K order of that product is permuted to match (tokens 4g..4g+3 and
-// 16+4g..16+4g+3 for lane group g); the V operand is read with the same
-// permutation, so P never leaves its registers.
+// A workgroup of NW waves takes one query row (wave w owns HT tiles of 16
+// heads, so heads = 16*HT*NW) and a contiguous range of its selected slots,
+// processed 32 at a time:
+//   * gather: the 32 selected 1152-byte key rows go straight into an LDS tile
+//     with 16-byte global->LDS loads (row pitch 1168 bytes spreads the LDS
+//     banks).  Tiles are double buffered and the rows they read were resolved
+//     two tiles earlier into a small LDS ring (index -> page -> row), so the
+//     loads of tile i+1 issue back to back while tile i is computed;
+//   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
+//       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
+//       registers for the whole launch; each LDS fragment feeds every head
+//       tile of the wave);
+//   * online softmax per head in the exp2 domain.  A head's reference max
+//     only moves when a tile's max exceeds it by more than 8 (so the
+//     unnormalised terms stay below 2^8); only then are its O rows and
+//     denominator rescaled, which keeps the rescale out of the steady state;
+//   * O[16 heads x 512] += P[16 x 32] . V[32 x 512] per head tile.  The S^T
+//     accumulator of lane (g, head) holds tokens 4g+i of each 16-token half,
+//     which is the A-operand slot set of the PV product once its K order is
+//     permuted to match (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group
+//     g); V is read with the same permutation by LDS transpose reads, so P
+//     never leaves its registers.
 // With more than one slot range per row (decode: few rows), each range
 // writes a normalised fp32 partial and its lse, merged by mla_combine.
 // --------------------------------------------------------------------------
 constexpr int kD = 576;
 constexpr int kDv = 512;
+constexpr int kKs = kD / 32;                   // 18 K-steps of the QK product
+constexpr int kNt = kDv / 16;                  // 32 output dim tiles
 constexpr int kBlk = 32;                       // selected tokens per tile
 constexpr int kRowBytes = kD * 2;              // 1152
 constexpr int kRowSlots = kRowBytes / 16 + 1;  // 72 data chunks + 1 pad chunk
 constexpr int kRowStride = kRowSlots * 16;     // 1168-byte LDS row pitch
 constexpr int kTileSlots = kBlk * kRowSlots;   // 2336 16-byte slots
-constexpr int kTileLoads = (kTileSlots + 63) / 64;     // wave-wide loads per tile
-constexpr int kTileBytes = kTileLoads * 64 * 16;       // rounded up to whole loads
+constexpr int kTileLoads = (kTileSlots + 63) / 64;  // wave-wide loads per tile
+constexpr int kTileBytes = kTileLoads * 64 * 16;    // rounded up to whole loads
+constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
 
-template <int NW>
 struct MlaLds {
   uint8_t tile[2][kTileBytes];
-  int32_t valid[2][kBlk];
+  int32_t rows[3][kBlk];  // resolved rows of tiles i, i+1, i+2 (-1: masked slot)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-template <int NW>
+template <int NW, int HT>
 __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     BatchDev bt, KeysDev kd, const __hip_bfloat16 *__restrict__ q,
     const __hip_bfloat16 *__restrict__ kv, const int32_t *__restrict__ idx, int k,
     int slots_per_split, float sm_scale, __hip_bfloat16 *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse) {
-  constexpr int H = NW * 16;
-  __shared__ MlaLds<NW> sh;
+  constexpr int HW = 16 * HT;  // heads per wave
+  constexpr int H = HW * NW;
+  __shared__ MlaLds sh;
 
   const int t = blockIdx.x;
   const int split = blockIdx.y;
@@ -151,152 +161,189 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   const uint8_t *kv_bytes = (const uint8_t *)kv;
   const int64_t row0 = key_row(kd, b, 0);  // stand-in row for masked / pad slots
 
-  // query operand (B of S^T): head 16*wave + n16, dims 32*ks + 8g .. +8
-  v8bf qf[kD / 32];
-  {
-    const __hip_bfloat16 *qh = q + ((int64_t)t * H + 16 * wave + n16) * kD + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) qf[ks] = *(const v8bf *)(qh + 32 * ks);
-  }
-
-  // Gather of tile `blk` into buffer `buf`: wave-wide load j of wave w fills
-  // LDS slots 64*(NW*j + w) .. +63; slot -> (row = slot / 73, chunk = slot % 73),
-  // chunk 72 is pitch padding (reloads chunk 0), rows >= 32 are tail padding.
+  // row of slot `tid % 32` of tile blk, -1 when masked
+  auto resolve = [&](int blk) -> int32_t {
+    const int si = slot_begin + blk * kBlk + (tid & (kBlk - 1));
+    const int s = si < slot_end ? idx_t[si] : -1;
+    return s >= 0 ? (int32_t)key_row(kd, b, s) : -1;
+  };
+  // gather of tile blk into buffer buf: wave-wide load j of wave w fills LDS
+  // slots 64*(NW*j + w) .. +63; slot -> (row = slot / 73, chunk = slot % 73);
+  // chunk 72 is pitch padding and rows >= 32 tail padding (both reload chunk 0)
   auto gather = [&](int blk, int buf) {
+    const int32_t *rows = sh.rows[blk % 3];
     for (int j = 0; NW * j + wave < kTileLoads; ++j) {
       const int base = 64 * (NW * j + wave);
       const int slot = base + lane;
       const int r = slot / kRowSlots;
       int c = slot - r * kRowSlots;
-      int64_t row = row0;
-      if (r < kBlk) {
-        const int si = slot_begin + blk * kBlk + r;
-        const int s = si < slot_end ? idx_t[si] : -1;
-        if (s >= 0) row = key_row(kd, b, s);
-      }
+      int64_t row = r < kBlk ? rows[r] : -1;
+      if (row < 0) row = row0;
       if (c == kRowSlots - 1 || r >= kBlk) c = 0;
       __builtin_amdgcn_global_load_lds((const void *)(kv_bytes + row * kRowBytes + c * 16),
                                        (lds_void *)(&sh.tile[buf][base * 16]), 16, 0, 0);
     }
-    if (tid < kBlk) {
-      const int si = slot_begin + blk * kBlk + tid;
-      sh.valid[buf][tid] = si < slot_end && idx_t[si] >= 0;
-    }
   };
 
-  v4f o_acc[kDv / 16];
+  // query operand (B of S^T): heads HW*w + 16*ht + n16, dims 32*ks + 8g .. +8
+  v8bf qf[HT][kKs];
 #pragma unroll
-  for (int i = 0; i < kDv / 16; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of this lane's head (log2 domain)
-  float l_part = 0.f;       // this lane's share of the running denominator
+  for (int ht = 0; ht < HT; ++ht) {
+    const __hip_bfloat16 *qh = q + ((int64_t)t * H + HW * wave + 16 * ht + n16) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qf[ht][ks] = *(const v8bf *)(qh + 32 * ks);
+  }
+
+  v4f o[HT][kNt];
+  float m_ref[HT], l_part[HT];  // reference max (log2 domain), this lane's denominator share
   const float zscale = sm_scale * kLog2e;
 
-  if (nblk > 0) gather(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1;
-    if (blk + 1 < nblk) gather(blk + 1, buf ^ 1);
-    const uint8_t *tile = sh.tile[buf];
-
-    // ---- S^T = KV . Q^T for two 16-token halves ----
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  {
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) {
-      const v8bf a0 = *(const v8bf *)(tile + n16 * kRowStride + 64 * ks + 16 * g);
-      const v8bf a1 = *(const v8bf *)(tile + (16 + n16) * kRowStride + 64 * ks + 16 * g);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+    for (int ht = 0; ht < HT; ++ht) {
+      m_ref[ht] = -INFINITY;
+      l_part[ht] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNt; ++i) o[ht][i] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-
-    // ---- online softmax (this lane: head n16, tokens 4g+i and 16+4g+i) ----
-    float z[8];
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = sh.valid[buf][4 * g + i] ? s0[i] * zscale : -INFINITY;
-      z[4 + i] = sh.valid[buf][16 + 4 * g + i] ? s1[i] * zscale : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zmax = fmaxf(zmax, z[i]);
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-    const float m_new = fmaxf(m_run, zmax);
-    float alpha = 1.f;
-    float p[8];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = exp2f(z[i] - m_new);
-    }
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) psum += p[i];
-    l_part = l_part * alpha + psum;
-
-    // rescale O rows (heads 4g+i of this lane's O tiles) when any max moved
-    if (__ballot(alpha != 1.f)) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-      for (int nt = 0; nt < kDv / 16; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o_acc[nt][i] *= al[i];
-    }
-
-    // ---- O += P . V ----
-    v8bf pa;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pa[i] = (__bf16)p[i];
-    // V operand by LDS transpose reads: inside a 16-lane group, lane i names
-    // 8 bytes of row i/4 (dims 4*(i%4)..+3 of the tile's 16); the read hands
-    // lane i column i of the four rows, i.e. 4 consecutive tokens of dim i.
-    const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kRowStride + 8 * (n16 & 3);
-#pragma unroll 8
-    for (int nt = 0; nt < kDv / 16; ++nt) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kRowStride + 32 * nt));
-      v8bf vb;
-      __builtin_memcpy(&vb, &lo, 8);
-      __builtin_memcpy((char *)&vb + 8, &hi, 8);
-      o_acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o_acc[nt], 0, 0, 0);
-    }
-
+    // prologue: resolve tiles 0 and 1, gather tile 0
+    if (tid < kBlk && nblk > 0) sh.rows[0][tid] = resolve(0);
+    if (tid >= kBlk && tid < 2 * kBlk && nblk > 1) sh.rows[1][tid - kBlk] = resolve(1);
+    __syncthreads();
+    if (nblk > 0) gather(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+
+    for (int blk = 0; blk < nblk; ++blk) {
+      const int buf = blk & 1;
+      int32_t ahead = -1;
+      if (tid < kBlk && blk + 2 < nblk) ahead = resolve(blk + 2);
+      if (blk + 1 < nblk) gather(blk + 1, buf ^ 1);
+      const uint8_t *tile = sh.tile[buf];
+      const int32_t *rows = sh.rows[blk % 3];
+
+      // ---- S^T = KV . Q^T: tokens 0-15 / 16-31 x each head tile ----
+      v4f s0[HT], s1[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        s0[ht] = v4f{0.f, 0.f, 0.f, 0.f};
+        s1[ht] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+      const uint8_t *arow = tile + n16 * kRowStride + 16 * g;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        const v8bf a0 = *(const v8bf *)(arow + 64 * ks);
+        const v8bf a1 = *(const v8bf *)(arow + 16 * kRowStride + 64 * ks);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          s0[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ht][ks], s0[ht], 0, 0, 0);
+          s1[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ht][ks], s1[ht], 0, 0, 0);
+        }
+      }
+
+      // ---- softmax terms (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
+      bool ok[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ok[i] = rows[4 * g + i] >= 0;
+        ok[4 + i] = rows[16 + 4 * g + i] >= 0;
+      }
+      v8bf pf[HT];
+      bool rescale = false;
+      float alpha[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float z[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
+          z[4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
+        }
+        float x = z[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) x = fmaxf(x, z[i]);
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        const float m_new = x > m_ref[ht] + kRefSlack ? x : m_ref[ht];
+        alpha[ht] = m_new == m_ref[ht] ? 1.f : exp2f(m_ref[ht] - m_new);
+        rescale |= alpha[ht] != 1.f;
+        m_ref[ht] = m_new;
+        l_part[ht] *= alpha[ht];
+        const float mr = m_ref[ht];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pv = mr == -INFINITY ? 0.f : exp2f(z[i] - mr);
+          sum += pv;
+          pf[ht][i] = (__bf16)pv;
+        }
+        l_part[ht] += sum;
+      }
+      if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          float r[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = __shfl(alpha[ht], 4 * g + i, 64);
+#pragma unroll
+          for (int nt = 0; nt < kNt; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[ht][nt][i] *= r[i];
+        }
+      }
+
+      // ---- O += P . V ----
+      // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
+      // of a 16-dim tile); the transpose read hands lane i column i of the four
+      // rows: 4 consecutive tokens of one dim, the B-operand slot order
+      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kRowStride + 8 * (n16 & 3);
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kRowStride + 32 * nt));
+        v8bf vb;
+        __builtin_memcpy(&vb, &lo, 8);
+        __builtin_memcpy((char *)&vb + 8, &hi, 8);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
+      }
+
+      __builtin_amdgcn_s_waitcnt(0);
+      if (tid < kBlk && blk + 2 < nblk) sh.rows[(blk + 2) % 3][tid] = ahead;
+      __syncthreads();
+    }
   }
 
   // ---- finish: denominators, output ----
-  float l_tot = l_part;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  // lanes n16 = head hold (m_run, l_tot) of head 16*wave + n16
-  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_head = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  float inv_row[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) inv_row[i] = __shfl(inv_l, 4 * g + i, 64);
-  const int h0 = 16 * wave + 4 * g;  // first head of this lane's O rows
-  if (nsplit == 1) {
+  for (int ht = 0; ht < HT; ++ht) {
+    float lt = l_part[ht];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    // lane n16 holds (m, l) of head HW*w + 16*ht + n16
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_h = lt > 0.f ? (m_ref[ht] + log2f(lt)) * kLn2 : -INFINITY;
+    float ir[4];
 #pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt)
+    for (int i = 0; i < 4; ++i) ir[i] = __shfl(inv, 4 * g + i, 64);
+    const int h0 = HW * wave + 16 * ht + 4 * g;  // first head of this lane's O rows
+    if (nsplit == 1) {
+      __hip_bfloat16 *ot = out + (int64_t)t * H * kDv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        out[((int64_t)t * H + h0 + i) * kDv + 16 * nt + n16] =
-            __float2bfloat16(o_acc[nt][i] * inv_row[i]);
-    if (lse && g == 0) lse[(int64_t)t * H + 16 * wave + n16] = lse_head;
-  } else {
-    float *po = part_o + ((int64_t)t * nsplit + split) * H * kDv;
+      for (int nt = 0; nt < kNt; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < kDv / 16; ++nt)
+        for (int i = 0; i < 4; ++i)
+          ot[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = __float2bfloat16(o[ht][nt][i] * ir[i]);
+      if (lse && g == 0) lse[(int64_t)t * H + HW * wave + 16 * ht + n16] = lse_h;
+    } else {
+      float *po = part_o + ((int64_t)t * nsplit + split) * H * kDv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = o_acc[nt][i] * inv_row[i];
-    if (g == 0) part_lse[((int64_t)t * nsplit + split) * H + 16 * wave + n16] = lse_head;
+      for (int nt = 0; nt < kNt; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = o[ht][nt][i] * ir[i];
+      if (g == 0) part_lse[((int64_t)t * nsplit + split) * H + HW * wave + 16 * ht + n16] = lse_h;
+    }
   }
 }
 
@@ -371,17 +418,17 @@ hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_querie
   const dim3 grid(num_queries, nsplit);
   switch (heads) {
     case 128:
-      hipLaunchKernelGGL(mla_bf16_kernel<8>, grid, dim3(512), 0, stream, bt, kd,
+      hipLaunchKernelGGL((mla_bf16_kernel<8, 1>), grid, dim3(512), 0, stream, bt, kd,
                          (const __hip_bfloat16 *)q, (const __hip_bfloat16 *)kv, indices, k, per,
                          sm_scale, (__hip_bfloat16 *)out, lse, part_o, part_lse);
       break;
     case 64:
-      hipLaunchKernelGGL(mla_bf16_kernel<4>, grid, dim3(256), 0, stream, bt, kd,
+      hipLaunchKernelGGL((mla_bf16_kernel<4, 1>), grid, dim3(256), 0, stream, bt, kd,
                          (const __hip_bfloat16 *)q, (const __hip_bfloat16 *)kv, indices, k, per,
                          sm_scale, (__hip_bfloat16 *)out, lse, part_o, part_lse);
       break;
     case 16:
-      hipLaunchKernelGGL(mla_bf16_kernel<1>, grid, dim3(64), 0, stream, bt, kd,
+      hipLaunchKernelGGL((mla_bf16_kernel<1, 1>), grid, dim3(64), 0, stream, bt, kd,
                          (const __hip_bfloat16 *)q, (const __hip_bfloat16 *)kv, indices, k, per,
                          sm_scale, (__hip_bfloat16 *)out, lse, part_o, part_lse);
       break;
