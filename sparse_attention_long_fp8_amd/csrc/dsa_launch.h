@@ -16,10 +16,11 @@ hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_que
                               const float *k, float scale, float *scores, int64_t ld,
                               hipStream_t stream);
 
-hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_queries,
-                              int max_k_len, int h_i, const uint8_t *q, const float *q_scale,
-                              const float *w, const uint8_t *k, const float *k_scale, float scale,
-                              float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
+                              int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,
+                              const float *q_scale, const float *w, const uint8_t *k,
+                              const float *k_scale, float scale, float *scores, int64_t ld,
+                              hipStream_t stream);
 
 hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
                        int k, int32_t *indices, hipStream_t stream);

@@ -88,13 +88,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       a[mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
-  // head weights of the accumulator rows this lane holds
+  // head weights of the accumulator rows this lane holds (rows 8r + 4*half + 0..3)
   float wr[MT][16];
   const float *wt = w + (int64_t)t * H;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wr[mt][i] = wt[32 * mt + 8 * (i / 4) + 4 * half + (i % 4)];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 v = *(const float4 *)(wt + 32 * mt + 8 * r4 + 4 * half);
+      wr[mt][4 * r4 + 0] = v.x;
+      wr[mt][4 * r4 + 1] = v.y;
+      wr[mt][4 * r4 + 2] = v.z;
+      wr[mt][4 * r4 + 3] = v.w;
+    }
   const float row_scale = q_scale[t] * scale;
   float *out = scores + (int64_t)t * ld;
 
@@ -130,6 +136,154 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
 }
 
 // --------------------------------------------------------------------------
+// FP8 E4M3 path for many query rows per sequence (prefill, chunked prefill).
+//
+// A workgroup of 4 waves takes QT = 4*QW consecutive query rows of one
+// sequence (wave w owns rows QW*w .. QW*w+QW-1) and a chunk of that
+// sequence's keys.  Keys are staged 64 at a time into LDS with 16-byte
+// global->LDS loads (each wave-wide load covers 8 whole key rows, 1 KiB of
+// contiguous memory), double buffered, so every key byte crosses HBM/L2 once
+// per workgroup instead of once per query row.  Chunk c of key r is stored at
+// slot 8r + (c ^ ((r >> 1) & 7)): the XOR spreads the 32 rows a B-fragment
+// read touches over distinct LDS banks.  Per wave and 32-key subtile, the
+// staged fragments feed QW rows x MT head tiles of 32x32x64 MFMAs; ReLU,
+// head weights and the head sum happen on the accumulators as in the
+// single-row kernel.  Keys at or beyond a row's candidate count are computed
+// (the tile is shared) but not stored; subtiles entirely beyond it are skipped.
+// --------------------------------------------------------------------------
+constexpr int kStageKeys = 64;
+constexpr int kStageBytes = kStageKeys * 128;
+
+typedef __attribute__((address_space(3))) void lds_void_i;
+
+template <int MT, int QW>
+__global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
+    BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const float *__restrict__ w, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld,
+    int keys_per_block) {
+  constexpr int H = 32 * MT;
+  constexpr int QT = 4 * QW;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+
+  const int b = blockIdx.z;
+  const int q0 = bt.q_seq_start[b];
+  const int nq = bt.q_seq_start[b + 1] - q0;
+  const int g0 = blockIdx.y * QT;  // first query of the group within the sequence
+  if (g0 >= nq) return;
+  const int kl = bt.k_len[b];
+  const int first_pos = kl - nq;  // position of the sequence's query 0
+  const int n_max = first_pos + min(nq, g0 + QT);  // candidates of the group's last row
+  const int s_begin = blockIdx.x * keys_per_block;
+  if (s_begin >= n_max) return;
+  const int s_end = min(n_max, s_begin + keys_per_block);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // rows of this wave: query index i within the sequence, candidates n
+  int row_t[QW], row_n[QW];
+  v8i a[QW][MT][2];
+  float wr[QW][MT][16];
+  float row_scale[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    const int i = g0 + QW * wave + j;
+    const bool live = i < nq;
+    const int t = q0 + (live ? i : nq - 1);
+    row_t[j] = t;
+    row_n[j] = live ? first_pos + i + 1 : 0;
+    const uint8_t *qt = q + (int64_t)t * H * 128;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        a[j][mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
+    const float *wt = w + (int64_t)t * H;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = *(const float4 *)(wt + 32 * mt + 8 * r4 + 4 * half);
+        wr[j][mt][4 * r4 + 0] = v.x;
+        wr[j][mt][4 * r4 + 1] = v.y;
+        wr[j][mt][4 * r4 + 2] = v.z;
+        wr[j][mt][4 * r4 + 3] = v.w;
+      }
+    row_scale[j] = q_scale[t] * scale;
+  }
+
+  // stage keys [s0, s0 + 64): wave w issues wave-wide loads w and w + 4, each
+  // filling 64 slots = 8 key rows
+  auto stage_keys = [&](int s0, int buf) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = wave + 4 * jj;
+      const int r = 8 * j + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int s = min(s0 + r, n_max - 1);
+      const int64_t row = key_row(kd, b, s);
+      __builtin_amdgcn_global_load_lds((const void *)(k + row * 128 + 16 * c),
+                                       (lds_void_i *)(&stage[buf][64 * 16 * j]), 16, 0, 0);
+    }
+  };
+
+  const int nstage = (s_end - s_begin + kStageKeys - 1) / kStageKeys;
+  stage_keys(s_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int s0 = s_begin + st * kStageKeys;
+    const int buf = st & 1;
+    if (st + 1 < nstage) stage_keys(s0 + kStageKeys, buf ^ 1);
+    const uint8_t *sb = stage[buf];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sk0 = s0 + 32 * sub;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < QW; ++j) any |= sk0 < row_n[j];
+      if (!any) continue;  // uniform over the wave
+      // B fragments of keys sk0 .. sk0+31: lane key r = 32*sub + col,
+      // K-step ks holds chunks 4ks + 2*half and 4ks + 2*half + 1
+      const int r = 32 * sub + col;
+      const int swz = (r >> 1) & 7;
+      v8i bf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 4 * ks + 2 * half;
+        const v4i lo = *(const v4i *)(sb + 16 * (8 * r + (c0 ^ swz)));
+        const v4i hi = *(const v4i *)(sb + 16 * (8 * r + ((c0 + 1) ^ swz)));
+        bf[ks] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const int s = sk0 + col;
+      const float ksc = k_scale[key_row(kd, b, min(s, n_max - 1))];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        if (sk0 >= row_n[j]) continue;  // uniform over the wave
+        float sum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v16f acc = {};
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][0], bf[0], acc, 0, 0, 0, 127, 0, 127);
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][1], bf[1], acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], fmaxf(acc[i], 0.f), sum);
+        }
+        sum += __shfl_xor(sum, 32, 64);
+        if (half == 0 && s < row_n[j] && s < s_end)
+          scores[(int64_t)row_t[j] * ld + s] = sum * row_scale[j] * ksc;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
 hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_queries,
@@ -142,11 +296,21 @@ hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_que
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_queries,
-                              int max_k_len, int h_i, const uint8_t *q, const float *q_scale,
-                              const float *w, const uint8_t *k, const float *k_scale, float scale,
-                              float *scores, int64_t ld, hipStream_t stream) {
-  const int keys_per_block = kIdxTile * 4 * 4;  // 4 waves x 4 tiles
+hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
+                              int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,
+                              const float *q_scale, const float *w, const uint8_t *k,
+                              const float *k_scale, float scale, float *scores, int64_t ld,
+                              hipStream_t stream) {
+  if (max_q_per_seq >= 8 && h_i == 64) {
+    constexpr int QW = 2;
+    const int keys_per_block = 2048;
+    dim3 grid((max_k_len + keys_per_block - 1) / keys_per_block, (max_q_per_seq + 4 * QW - 1) / (4 * QW),
+              num_seqs);
+    hipLaunchKernelGGL((indexer_fp8_tiled_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                       q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+    return hipGetLastError();
+  }
+  const int keys_per_block = kIdxTile * 4 * 8;  // 4 waves x 8 tiles
   dim3 grid((max_k_len + keys_per_block - 1) / keys_per_block, num_queries);
   switch (h_i / 32) {
     case 1:

@@ -199,8 +199,9 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t *batch, const dsa_kv_layout_t 
   const dsa::KeysDev kd = to_dev(keys);
   hipError_t e;
   if (dtype == DSA_FP8_E4M3)
-    e = dsa::launch_indexer_fp8(bt, kd, batch->num_queries, batch->max_k_len, h_i, (const uint8_t *)q_idx, q_scale,
-                                w, (const uint8_t *)k_idx, k_scale, scale, scores, ld_scores, stream);
+    e = dsa::launch_indexer_fp8(bt, kd, batch->num_seqs, batch->num_queries, batch->max_q_per_seq, batch->max_k_len,
+                                h_i, (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scale,
+                                scores, ld_scores, stream);
   else
     e = dsa::launch_indexer_f32(bt, kd, batch->num_queries, batch->max_k_len, h_i, d_i, (const float *)q_idx, w,
                                 (const float *)k_idx, scale, scores, ld_scores, stream);
