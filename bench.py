@@ -175,6 +175,7 @@ def main():
         return
     from sparse_attention_long_fp8_amd import binding as B
     from sparse_attention_long_fp8_amd import synth
+    from sparse_attention_long_fp8_amd.workload import DeviceWorkload
 
     wl = synth.WORKLOADS[args.workload]
     decode = wl.kind != "prefill"
@@ -184,90 +185,16 @@ def main():
     dev = torch.device("cuda:0")
     B.lib()  # fail loudly now if the library is missing
 
-    s = synth.Synth(wl)
-    lay = s.layout
-    T, N = lay.num_queries, int(lay.k_seq_start[-1])
-    print("[bench] %s: generating inputs (T=%d, keys=%d)" % (wl.name, T, N), file=sys.stderr, flush=True)
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
 
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-
-    def upload_bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    q_seq_start, k_len = i32(lay.q_seq_start), i32(lay.k_len)
-    k_seq_start = torch.from_numpy(lay.k_seq_start[:-1].astype(np.int64)).to(dev)
-    batch = B.make_batch(q_seq_start, k_len, wl.batch, T, lay.max_q_per_seq, lay.max_k_len)
-    ld = (lay.max_k_len + 3) // 4 * 4
-    dt_q = torch.bfloat16 if wl.fp8 else torch.float32
-    # inputs, generated in slabs straight into device tensors
-    qi = torch.empty((T, wl.h_i, wl.d_i), dtype=torch.uint8 if wl.fp8 else torch.float32, device=dev)
-    qs = torch.empty(T, dtype=torch.float32, device=dev) if wl.fp8 else None
-    w = torch.empty((T, wl.h_i), dtype=torch.float32, device=dev)
-    q = torch.empty((T, wl.heads, wl.d_qk), dtype=dt_q, device=dev)
-    slab = 2048
-    for r0 in range(0, T, slab):
-        r1 = min(T, r0 + slab)
-        c, sc = s.qi(r0, r1)
-        qi[r0:r1] = torch.from_numpy(c).to(dev)
-        if wl.fp8:
-            qs[r0:r1] = torch.from_numpy(sc).to(dev)
-        w[r0:r1] = torch.from_numpy(s.w(r0, r1)).to(dev)
-        qq = s.q(r0, r1)
-        q[r0:r1] = upload_bf16(qq) if wl.fp8 else torch.from_numpy(qq).to(dev)
-    if wl.paged:
-        ki_pool, ks_pool, kv_pool = s.paged_pools()
-        ki = torch.from_numpy(ki_pool).to(dev)
-        ks = torch.from_numpy(ks_pool).to(dev)
-        kv = upload_bf16(kv_pool)
-        page_table = i32(lay.page_table)
-        layout = B.make_paged_layout(page_table, lay.page_table.shape[1], lay.num_pages)
-    else:
-        ki = torch.empty((N, wl.d_i), dtype=torch.uint8 if wl.fp8 else torch.float32, device=dev)
-        ks = torch.empty(N, dtype=torch.float32, device=dev) if wl.fp8 else None
-        kv = torch.empty((N, wl.d_qk), dtype=dt_q, device=dev)
-        for g0 in range(0, N, 65536):
-            g1 = min(N, g0 + 65536)
-            c, sc = s.ki(g0, g1)
-            ki[g0:g1] = torch.from_numpy(c).to(dev)
-            if wl.fp8:
-                ks[g0:g1] = torch.from_numpy(sc).to(dev)
-            kk = s.kv(g0, g1)
-            kv[g0:g1] = upload_bf16(kk) if wl.fp8 else torch.from_numpy(kk).to(dev)
-        layout = B.make_contiguous_layout(k_seq_start, N)
-    sets = [(qi, qs, w, q, ki, ks, kv)]
-    for _ in range(copies - 1):
-        sets.append(tuple(None if x is None else x.clone() for x in sets[0]))
-    index_dtype = B.DSA_FP8_E4M3 if wl.fp8 else B.DSA_F32
-    mla_dtype = B.DSA_BF16 if wl.fp8 else B.DSA_F32
-    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
-    out = torch.empty((T, wl.heads, wl.d_v), dtype=dt_q, device=dev)
-    lse = torch.empty((T, wl.heads), dtype=torch.float32, device=dev)
-    ws_bytes = B.dsa_sparse_mla_workspace_size(batch, mla_dtype, wl.heads, wl.d_qk, wl.d_v, wl.top_k)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    dw = DeviceWorkload(wl, dev, copies=copies, log=log)
+    lay, T = dw.lay, dw.T
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        qi_, qs_, w_, q_, ki_, ks_, kv_ = sets[i % copies]
-        if ev:
-            ev[0].record(stream)
-        B.dsa_indexer_scores(batch, layout, index_dtype, wl.h_i, wl.d_i, qi_, qs_, w_, ki_, ks_, wl.index_scale,
-                             scores, ld, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        B.dsa_topk(batch, scores, ld, wl.top_k, idx, stream=stream)
-        if ev:
-            ev[2].record(stream)
-        B.dsa_sparse_mla_fwd(batch, layout, mla_dtype, wl.heads, wl.d_qk, wl.d_v, q_, kv_, idx, wl.top_k,
-                             wl.sm_scale, out, lse, ws, ws_bytes, stream=stream)
-        if ev:
-            ev[3].record(stream)
-
-    print("[bench] warmup %d, timed %d steps, %d input copies" % (warmup, steps, copies), file=sys.stderr,
-          flush=True)
+    log("warmup %d, timed %d steps, %d input copies" % (warmup, steps, copies))
     for i in range(warmup):
-        step(i)
+        dw.step(i, stream)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -275,7 +202,7 @@ def main():
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(steps):
-        step(warmup + i, evs[i])
+        dw.step(warmup + i, stream, evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
@@ -326,7 +253,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (budget %.0f s)" % args.cpu_budget, file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, s, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, dw.synth, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
