@@ -66,6 +66,48 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// 16-byte global -> LDS load for a whole wave: lane i's 16 bytes land at LDS
+// byte offset lds_base + 16 * i (lds_base must be wave-uniform).  Written as
+// inline assembly so that the compiler does not treat every later LDS read as
+// possibly aliasing it (it would otherwise drain all such loads before them);
+// callers wait for completion with an explicit vmcnt wait.  M0, which carries
+// the LDS base, is saved and restored inside the block.
+__device__ __forceinline__ void lds_dma16(const void *gaddr, void *lds_dst_wave) {
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t *)lds_dst_wave);
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(gaddr)
+      : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also fences
+// global memory, i.e. waits for every outstanding vector-memory operation,
+// which would retire loads deliberately kept in flight across the barrier.
+// Callers have already waited for the loads the next step reads, so only this
+// wave's own LDS operations need to complete before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Exclusive count of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

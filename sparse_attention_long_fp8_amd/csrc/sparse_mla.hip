@@ -90,13 +90,15 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, in
 // bf16 path: d_qk = 576 (512 latent + 64 rotary), d_v = 512.
 //
 // A workgroup of NW waves takes one query row (wave w owns HT tiles of 16
-// heads, so heads = 16*HT*NW) and a contiguous range of its selected slots,
-// processed 32 at a time:
-//   * gather: the 32 selected 1152-byte key rows go straight into an LDS tile
-//     with 16-byte global->LDS loads (row pitch 1168 bytes spreads the LDS
-//     banks).  Tiles are double buffered and the rows they read were resolved
-//     two tiles earlier into a small LDS ring (index -> page -> row), so the
-//     loads of tile i+1 issue back to back while tile i is computed;
+// heads, so heads = 16*HT*NW) and a contiguous range of at most 2048 of its
+// selected slots, processed 32 at a time:
+//   * rows: every slot of the range is resolved once (index -> page -> row)
+//     into LDS before the tile loop, so the loop issues no dependent loads;
+//   * gather: the 32 selected 1152-byte key rows of a tile go straight into
+//     LDS with 16-byte global->LDS loads (row pitch 1168 bytes spreads the LDS
+//     banks).  Three tile buffers keep two tiles in flight while one is
+//     computed; every wave issues exactly kLoadsPerWave loads per tile, so a
+//     per-wave vmcnt wait retires exactly the tile that is needed next;
 //   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
 //       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
 //       registers for the whole launch; each LDS fragment feeds every head
@@ -112,24 +114,27 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, in
 //     g); V is read with the same permutation by LDS transpose reads, so P
 //     never leaves its registers.
 // With more than one slot range per row (decode: few rows), each range
-// writes a normalised fp32 partial and its lse, merged by mla_combine.
+// writes its normalised output in bf16 plus its lse, merged by mla_combine.
 // --------------------------------------------------------------------------
 constexpr int kD = 576;
 constexpr int kDv = 512;
 constexpr int kKs = kD / 32;                   // 18 K-steps of the QK product
 constexpr int kNt = kDv / 16;                  // 32 output dim tiles
 constexpr int kBlk = 32;                       // selected tokens per tile
+constexpr int kMaxSlots = 2048;                // slots one workgroup resolves
 constexpr int kRowBytes = kD * 2;              // 1152
 constexpr int kRowSlots = kRowBytes / 16 + 1;  // 72 data chunks + 1 pad chunk
 constexpr int kRowStride = kRowSlots * 16;     // 1168-byte LDS row pitch
 constexpr int kTileSlots = kBlk * kRowSlots;   // 2336 16-byte slots
-constexpr int kTileLoads = (kTileSlots + 63) / 64;  // wave-wide loads per tile
-constexpr int kTileBytes = kTileLoads * 64 * 16;    // rounded up to whole loads
+constexpr int kTileLoads = 40;                 // wave-wide loads per tile (>= 2336/64, divisible by 8)
+constexpr int kTileBytes = kTileLoads * 64 * 16;
+constexpr int kBufs = 3;                       // tile buffers: one computed, two in flight
 constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
+static_assert(kTileLoads * 64 >= kTileSlots, "tile loads cover the tile");
 
 struct MlaLds {
-  uint8_t tile[2][kTileBytes];
-  int32_t rows[3][kBlk];  // resolved rows of tiles i, i+1, i+2 (-1: masked slot)
+  uint8_t tile[kBufs][kTileBytes];
+  int32_t rows[kMaxSlots];  // resolved rows of the range (-1: masked slot)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -140,9 +145,12 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     BatchDev bt, KeysDev kd, const __hip_bfloat16 *__restrict__ q,
     const __hip_bfloat16 *__restrict__ kv, const int32_t *__restrict__ idx, int k,
     int slots_per_split, float sm_scale, __hip_bfloat16 *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    float *__restrict__ lse, __hip_bfloat16 *__restrict__ part_o, float *__restrict__ part_lse) {
   constexpr int HW = 16 * HT;  // heads per wave
   constexpr int H = HW * NW;
+  constexpr int NT = NW * 64;
+  constexpr int kLoadsPerWave = kTileLoads / NW;
+  static_assert(kTileLoads % NW == 0, "every wave issues the same number of tile loads");
   __shared__ MlaLds sh;
 
   const int t = blockIdx.x;
@@ -156,34 +164,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   const int b = seq_of_row(bt, t);
   const int slot_begin = split * slots_per_split;
   const int slot_end = min(k, slot_begin + slots_per_split);
-  const int nblk = slot_end > slot_begin ? (slot_end - slot_begin + kBlk - 1) / kBlk : 0;
+  const int nslot = max(slot_end - slot_begin, 0);
+  const int nblk = (nslot + kBlk - 1) / kBlk;
   const int32_t *idx_t = idx + (int64_t)t * k;
   const uint8_t *kv_bytes = (const uint8_t *)kv;
   const int64_t row0 = key_row(kd, b, 0);  // stand-in row for masked / pad slots
-
-  // row of slot `tid % 32` of tile blk, -1 when masked
-  auto resolve = [&](int blk) -> int32_t {
-    const int si = slot_begin + blk * kBlk + (tid & (kBlk - 1));
-    const int s = si < slot_end ? idx_t[si] : -1;
-    return s >= 0 ? (int32_t)key_row(kd, b, s) : -1;
-  };
-  // gather of tile blk into buffer buf: wave-wide load j of wave w fills LDS
-  // slots 64*(NW*j + w) .. +63; slot -> (row = slot / 73, chunk = slot % 73);
-  // chunk 72 is pitch padding and rows >= 32 tail padding (both reload chunk 0)
-  auto gather = [&](int blk, int buf) {
-    const int32_t *rows = sh.rows[blk % 3];
-    for (int j = 0; NW * j + wave < kTileLoads; ++j) {
-      const int base = 64 * (NW * j + wave);
-      const int slot = base + lane;
-      const int r = slot / kRowSlots;
-      int c = slot - r * kRowSlots;
-      int64_t row = r < kBlk ? rows[r] : -1;
-      if (row < 0) row = row0;
-      if (c == kRowSlots - 1 || r >= kBlk) c = 0;
-      __builtin_amdgcn_global_load_lds((const void *)(kv_bytes + row * kRowBytes + c * 16),
-                                       (lds_void *)(&sh.tile[buf][base * 16]), 16, 0, 0);
-    }
-  };
 
   // query operand (B of S^T): heads HW*w + 16*ht + n16, dims 32*ks + 8g .. +8
   v8bf qf[HT][kKs];
@@ -193,126 +178,150 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) qf[ht][ks] = *(const v8bf *)(qh + 32 * ks);
   }
+  // resolve every slot of the range once
+  for (int i = tid; i < nblk * kBlk; i += NT) {
+    const int s = i < nslot ? idx_t[slot_begin + i] : -1;
+    sh.rows[i] = s >= 0 ? (int32_t)key_row(kd, b, s) : -1;
+  }
+  __syncthreads();
+
+  // tile blk -> buffer buf: wave-wide load j of wave w fills LDS slots
+  // 64*(NW*j + w) .. +63; slot -> (row = slot / 73, chunk = slot % 73); chunk
+  // 72 is pitch padding and rows >= 32 tail padding (both reload chunk 0)
+  auto gather = [&](int blk, int buf) {
+    const int32_t *rows = sh.rows + blk * kBlk;
+#pragma unroll 1
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int base = 64 * (NW * j + wave);
+      const int slot = base + lane;
+      const int r = slot / kRowSlots;
+      int c = slot - r * kRowSlots;
+      int64_t row = r < kBlk ? rows[r] : -1;
+      if (row < 0) row = row0;
+      if (c == kRowSlots - 1 || r >= kBlk) c = 0;
+      lds_dma16(kv_bytes + row * kRowBytes + c * 16, &sh.tile[buf][base * 16]);
+    }
+  };
 
   v4f o[HT][kNt];
   float m_ref[HT], l_part[HT];  // reference max (log2 domain), this lane's denominator share
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m_ref[ht] = -INFINITY;
+    l_part[ht] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNt; ++i) o[ht][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
   const float zscale = sm_scale * kLog2e;
 
-  {
+  // The query loads must be complete (and known complete to the compiler)
+  // before the tile loop: otherwise its wait bookkeeping re-waits for them in
+  // every iteration, draining the tile loads kept in flight.
+  wait_vmcnt<0>();
+  if (nblk > 0) gather(0, 0);
+  if (nblk > 1) {
+    gather(1, 1);
+    wait_vmcnt<kLoadsPerWave>();  // tile 0 (and the query operand) landed
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk % kBufs;
+    const bool ahead = blk + 2 < nblk;
+    if (ahead) gather(blk + 2, (blk + 2) % kBufs);
+    const uint8_t *tile = sh.tile[buf];
+    const int32_t *rows = sh.rows + blk * kBlk;
+
+    // ---- S^T = KV . Q^T: tokens 0-15 / 16-31 x each head tile ----
+    v4f s0[HT], s1[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      m_ref[ht] = -INFINITY;
-      l_part[ht] = 0.f;
-#pragma unroll
-      for (int i = 0; i < kNt; ++i) o[ht][i] = v4f{0.f, 0.f, 0.f, 0.f};
+      s0[ht] = v4f{0.f, 0.f, 0.f, 0.f};
+      s1[ht] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    // prologue: resolve tiles 0 and 1, gather tile 0
-    if (tid < kBlk && nblk > 0) sh.rows[0][tid] = resolve(0);
-    if (tid >= kBlk && tid < 2 * kBlk && nblk > 1) sh.rows[1][tid - kBlk] = resolve(1);
-    __syncthreads();
-    if (nblk > 0) gather(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int blk = 0; blk < nblk; ++blk) {
-      const int buf = blk & 1;
-      int32_t ahead = -1;
-      if (tid < kBlk && blk + 2 < nblk) ahead = resolve(blk + 2);
-      if (blk + 1 < nblk) gather(blk + 1, buf ^ 1);
-      const uint8_t *tile = sh.tile[buf];
-      const int32_t *rows = sh.rows[blk % 3];
-
-      // ---- S^T = KV . Q^T: tokens 0-15 / 16-31 x each head tile ----
-      v4f s0[HT], s1[HT];
+    const uint8_t *arow = tile + n16 * kRowStride + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      const v8bf a0 = *(const v8bf *)(arow + 64 * ks);
+      const v8bf a1 = *(const v8bf *)(arow + 16 * kRowStride + 64 * ks);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        s0[ht] = v4f{0.f, 0.f, 0.f, 0.f};
-        s1[ht] = v4f{0.f, 0.f, 0.f, 0.f};
+        s0[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ht][ks], s0[ht], 0, 0, 0);
+        s1[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ht][ks], s1[ht], 0, 0, 0);
       }
-      const uint8_t *arow = tile + n16 * kRowStride + 16 * g;
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const v8bf a0 = *(const v8bf *)(arow + 64 * ks);
-        const v8bf a1 = *(const v8bf *)(arow + 16 * kRowStride + 64 * ks);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          s0[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ht][ks], s0[ht], 0, 0, 0);
-          s1[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ht][ks], s1[ht], 0, 0, 0);
-        }
-      }
+    }
 
-      // ---- softmax terms (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
-      bool ok[8];
+    // ---- online softmax (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok[i] = rows[4 * g + i] >= 0;
+      ok[4 + i] = rows[16 + 4 * g + i] >= 0;
+    }
+    v8bf pf[HT];
+    float alpha[HT];
+    bool rescale = false;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float z[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ok[i] = rows[4 * g + i] >= 0;
-        ok[4 + i] = rows[16 + 4 * g + i] >= 0;
+        z[i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
+        z[4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
       }
-      v8bf pf[HT];
-      bool rescale = false;
-      float alpha[HT];
+      float x = z[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) x = fmaxf(x, z[i]);
+      x = fmaxf(x, __shfl_xor(x, 16, 64));
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      const float m_new = x > m_ref[ht] + kRefSlack ? x : m_ref[ht];
+      alpha[ht] = m_new == m_ref[ht] ? 1.f : exp2f(m_ref[ht] - m_new);
+      rescale |= alpha[ht] != 1.f;
+      m_ref[ht] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+        sum += pv;
+        pf[ht][i] = (__bf16)pv;
+      }
+      l_part[ht] = l_part[ht] * alpha[ht] + sum;
+    }
+    if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        float z[8];
+        float r[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
-          z[4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
-        }
-        float x = z[0];
+        for (int i = 0; i < 4; ++i) r[i] = __shfl(alpha[ht], 4 * g + i, 64);
 #pragma unroll
-        for (int i = 1; i < 8; ++i) x = fmaxf(x, z[i]);
-        x = fmaxf(x, __shfl_xor(x, 16, 64));
-        x = fmaxf(x, __shfl_xor(x, 32, 64));
-        const float m_new = x > m_ref[ht] + kRefSlack ? x : m_ref[ht];
-        alpha[ht] = m_new == m_ref[ht] ? 1.f : exp2f(m_ref[ht] - m_new);
-        rescale |= alpha[ht] != 1.f;
-        m_ref[ht] = m_new;
-        l_part[ht] *= alpha[ht];
-        const float mr = m_ref[ht];
-        float sum = 0.f;
+        for (int nt = 0; nt < kNt; ++nt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = mr == -INFINITY ? 0.f : exp2f(z[i] - mr);
-          sum += pv;
-          pf[ht][i] = (__bf16)pv;
-        }
-        l_part[ht] += sum;
+          for (int i = 0; i < 4; ++i) o[ht][nt][i] *= r[i];
       }
-      if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          float r[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = __shfl(alpha[ht], 4 * g + i, 64);
-#pragma unroll
-          for (int nt = 0; nt < kNt; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[ht][nt][i] *= r[i];
-        }
-      }
-
-      // ---- O += P . V ----
-      // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
-      // of a 16-dim tile); the transpose read hands lane i column i of the four
-      // rows: 4 consecutive tokens of one dim, the B-operand slot order
-      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kRowStride + 8 * (n16 & 3);
-#pragma unroll
-      for (int nt = 0; nt < kNt; ++nt) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kRowStride + 32 * nt));
-        v8bf vb;
-        __builtin_memcpy(&vb, &lo, 8);
-        __builtin_memcpy((char *)&vb + 8, &hi, 8);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
-      }
-
-      __builtin_amdgcn_s_waitcnt(0);
-      if (tid < kBlk && blk + 2 < nblk) sh.rows[(blk + 2) % 3][tid] = ahead;
-      __syncthreads();
     }
+
+    // ---- O += P . V ----
+    // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
+    // of a 16-dim tile); the transpose read hands lane i column i of the four
+    // rows: 4 consecutive tokens of one dim, the B-operand slot order
+    const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kRowStride + 8 * (n16 & 3);
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kRowStride + 32 * nt));
+      v8bf vb;
+      __builtin_memcpy(&vb, &lo, 8);
+      __builtin_memcpy((char *)&vb + 8, &hi, 8);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
+    }
+
+    // the next tile must have landed; the one after may stay in flight
+    if (ahead) wait_vmcnt<kLoadsPerWave>(); else wait_vmcnt<0>();
+    lds_barrier();
   }
 
   // ---- finish: denominators, output ----
@@ -328,50 +337,55 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) ir[i] = __shfl(inv, 4 * g + i, 64);
     const int h0 = HW * wave + 16 * ht + 4 * g;  // first head of this lane's O rows
-    if (nsplit == 1) {
-      __hip_bfloat16 *ot = out + (int64_t)t * H * kDv;
+    __hip_bfloat16 *ot = nsplit == 1 ? out + (int64_t)t * H * kDv
+                                     : part_o + ((int64_t)t * nsplit + split) * H * kDv;
 #pragma unroll
-      for (int nt = 0; nt < kNt; ++nt)
+    for (int nt = 0; nt < kNt; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ot[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = __float2bfloat16(o[ht][nt][i] * ir[i]);
-      if (lse && g == 0) lse[(int64_t)t * H + HW * wave + 16 * ht + n16] = lse_h;
-    } else {
-      float *po = part_o + ((int64_t)t * nsplit + split) * H * kDv;
-#pragma unroll
-      for (int nt = 0; nt < kNt; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) po[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = o[ht][nt][i] * ir[i];
-      if (g == 0) part_lse[((int64_t)t * nsplit + split) * H + HW * wave + 16 * ht + n16] = lse_h;
+      for (int i = 0; i < 4; ++i)
+        ot[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = __float2bfloat16(o[ht][nt][i] * ir[i]);
+    if (g == 0) {
+      if (nsplit == 1) {
+        if (lse) lse[(int64_t)t * H + HW * wave + 16 * ht + n16] = lse_h;
+      } else {
+        part_lse[((int64_t)t * nsplit + split) * H + HW * wave + 16 * ht + n16] = lse_h;
+      }
     }
   }
 }
 
 // Merge of split partials: lse = log sum_i e^{lse_i}, o = sum_i e^{lse_i - lse} o_i.
+// Block = 4 heads x 64 lanes; a lane owns 8 consecutive dims (16-byte loads).
+constexpr int kMaxSplits = 32;
+
 __global__ __launch_bounds__(256) void mla_combine_kernel(int heads, int nsplit,
-                                                          const float *__restrict__ part_o,
+                                                          const __hip_bfloat16 *__restrict__ part_o,
                                                           const float *__restrict__ part_lse,
                                                           __hip_bfloat16 *__restrict__ out,
                                                           float *__restrict__ lse) {
   const int t = blockIdx.x;
-  const int h = blockIdx.y;
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const int d0 = 8 * (threadIdx.x & 63);
+  if (h >= heads) return;
+  const float *pl = part_lse + (int64_t)t * nsplit * heads + h;
   float mx = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, part_lse[((int64_t)t * nsplit + i) * heads + h]);
+  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * heads]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  float wts[16];
   for (int i = 0; i < nsplit; ++i) {
-    const float li = part_lse[((int64_t)t * nsplit + i) * heads + h];
-    wts[i] = mx == -INFINITY ? 0.f : expf(li - mx);
-    wsum += wts[i];
+    const float li = pl[(int64_t)i * heads];
+    const float wi = mx == -INFINITY ? 0.f : expf(li - mx);
+    wsum += wi;
+    const v8bf v = *(const v8bf *)(part_o + (((int64_t)t * nsplit + i) * heads + h) * kDv + d0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, (float)v[j], acc[j]);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int d = threadIdx.x; d < kDv; d += 256) {
-    float acc = 0.f;
-    for (int i = 0; i < nsplit; ++i)
-      acc += wts[i] * part_o[(((int64_t)t * nsplit + i) * heads + h) * kDv + d];
-    out[((int64_t)t * heads + h) * kDv + d] = __float2bfloat16(acc * inv);
-  }
-  if (lse && threadIdx.x == 0) lse[(int64_t)t * heads + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  v8bf r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)(acc[j] * inv);
+  *(v8bf *)(out + ((int64_t)t * heads + h) * kDv + d0) = r;
+  if (lse && d0 == 0) lse[(int64_t)t * heads + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 // --------------------------------------------------------------------------
@@ -390,17 +404,21 @@ hipError_t launch_mla_f32(const BatchDev &bt, const KeysDev &kd, int num_queries
 int mla_bf16_splits(int num_queries, int heads, int k) {
   (void)heads;
   if (num_queries <= 0) return 1;
-  int s = (256 + num_queries - 1) / num_queries;  // aim for one workgroup per CU
-  int max_s = (k + 4 * kBlk - 1) / (4 * kBlk);    // at least 4 tiles per split
+  const int min_s = (k + kMaxSlots - 1) / kMaxSlots;  // a range resolves at most 2048 slots
+  int s = (256 + num_queries - 1) / num_queries;      // aim for one workgroup per CU
+  const int max_s = (k + 4 * kBlk - 1) / (4 * kBlk);  // at least 4 tiles per range
   if (s > max_s) s = max_s;
-  if (s > 16) s = 16;
+  if (s < min_s) s = min_s;
+  if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : s;
 }
 
 size_t mla_bf16_workspace_bytes(int num_queries, int heads, int d_v, int k) {
   const int s = mla_bf16_splits(num_queries, heads, k);
   if (s <= 1) return 0;
-  return (size_t)num_queries * s * heads * ((size_t)d_v + 1) * sizeof(float);
+  // bf16 partial outputs, then fp32 partial lse (16-byte aligned)
+  const size_t po = ((size_t)num_queries * s * heads * d_v * 2 + 15) / 16 * 16;
+  return po + (size_t)num_queries * s * heads * sizeof(float);
 }
 
 hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
@@ -410,10 +428,13 @@ hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_querie
   if (num_queries == 0) return hipSuccess;
   const int nsplit = mla_bf16_splits(num_queries, heads, k);
   const int per = ((k + nsplit - 1) / nsplit + kBlk - 1) / kBlk * kBlk;
-  float *part_o = nullptr, *part_lse = nullptr;
+  if (per > kMaxSlots) return hipErrorInvalidValue;
+  __hip_bfloat16 *part_o = nullptr;
+  float *part_lse = nullptr;
   if (nsplit > 1) {
-    part_o = (float *)workspace;
-    part_lse = part_o + (size_t)num_queries * nsplit * heads * kDv;
+    part_o = (__hip_bfloat16 *)workspace;
+    const size_t po = ((size_t)num_queries * nsplit * heads * kDv * 2 + 15) / 16 * 16;
+    part_lse = (float *)((char *)workspace + po);
   }
   const dim3 grid(num_queries, nsplit);
   switch (heads) {
@@ -437,7 +458,7 @@ hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_querie
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(num_queries, heads), dim3(256), 0, stream, heads,
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(num_queries, (heads + 3) / 4), dim3(256), 0, stream, heads,
                      nsplit, part_o, part_lse, (__hip_bfloat16 *)out, lse);
   return hipGetLastError();
 }
