@@ -60,19 +60,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Wave 0 only.  Finds the bin d such that the count strictly above d is
-// < need and the count from d upward is >= need.  Lane l sums the l-th
-// group of nbins/64 bins counted from the top; an inclusive lane scan picks
-// the group, whose lane then walks its bins.
+// < need and the count from d upward is >= need.  Two wave-wide scans: lane l
+// first sums the l-th group of nbins/64 bins counted from the top and an
+// inclusive lane scan picks the group; then the group's bins, one per lane,
+// are scanned the same way.
 __device__ void scan_from_top(const uint32_t *hist, int nbins, int need, int32_t *out_bin,
                               int32_t *out_above) {
   const int lane = lane_id();
   const int c = nbins / 64;
   const int hi = nbins - lane * c;
   int s = 0;
-  for (int j = 1; j <= c; ++j) s += (int)hist[hi - j];
+  // lane l reads its group in the rotated order (j + l) % c, so that at every
+  // step the wave's 64 reads fall into distinct LDS banks
+  for (int j = 0; j < c; ++j) s += (int)hist[hi - 1 - ((j + lane) & (c - 1))];
   int incl = s;
   for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(incl, off, 64);
+    const int y = __shfl_up(incl, off, 64);
     if (lane >= off) incl += y;
   }
   const uint64_t hit = __ballot(incl >= need);
@@ -80,17 +83,34 @@ __device__ void scan_from_top(const uint32_t *hist, int nbins, int need, int32_t
     if (lane == 0) { *out_bin = 0; *out_above = 0; }
     return;
   }
-  const int first = __ffsll((unsigned long long)hit) - 1;
-  if (lane == first) {
-    int run = incl - s;
-    int bin = hi - c, above = run;
-    for (int j = 1; j <= c; ++j) {
-      int h = (int)hist[hi - j];
-      if (run + h >= need) { bin = hi - j; above = run; break; }
-      run += h;
-    }
-    *out_bin = bin;
+  const int grp = __ffsll((unsigned long long)hit) - 1;
+  const int above_grp = __shfl(incl - s, grp, 64);
+  const int top = nbins - grp * c;  // one past the group's highest bin
+  const int v = lane < c ? (int)hist[top - 1 - lane] : 0;
+  int incl2 = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl2, off, 64);
+    if (lane >= off) incl2 += y;
+  }
+  const uint64_t hit2 = __ballot(lane < c && above_grp + incl2 >= need);
+  const int j = hit2 ? __ffsll((unsigned long long)hit2) - 1 : c - 1;  // empty only with NaN scores
+  const int above = above_grp + __shfl(incl2 - v, j, 64);
+  if (lane == 0) {
+    *out_bin = top - 1 - j;
     *out_above = above;
+  }
+}
+
+// Loads of one sweep chunk: kU float4 per thread, all issued before any is
+// used (a plain loop would wait out one memory latency per load).
+constexpr int kU = 8;
+constexpr int kChunk = 4 * kU * kTkThreads;  // elements per sweep chunk (32768)
+
+__device__ __forceinline__ void load_chunk(const float *src, int base, int n, float4 (&v)[kU]) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int i = base + 4 * ((int)threadIdx.x + u * kTkThreads);
+    v[u] = i < n ? *(const float4 *)(src + i) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
@@ -113,29 +133,35 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   }
   const float *row = scores + (int64_t)t * ld;
   const bool cached = n <= kTkCache;
-  auto load4 = [&](int i) -> float4 {
-    return cached ? *(const float4 *)(&sh.cache[i]) : *(const float4 *)(row + i);
-  };
+  // every sweep after the first reads the LDS copy when the row fits
+#define DSA_SWEEP_CHUNK(base, v)              \
+  if (cached) load_chunk(sh.cache, base, n, v); \
+  else load_chunk(row, base, n, v);
 
   // ---- 1. cache the row, min / max key ----
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
-    float4 v = *(const float4 *)(row + i);
-    if (cached) *(float4 *)(&sh.cache[i]) = v;
-    const float f[4] = {v.x, v.y, v.z, v.w};
+  for (int base = 0; base < n; base += kChunk) {
+    float4 v[kU];
+    load_chunk(row, base, n, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + j < n) {
-        uint32_t key = float_key(f[j]);
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + 4 * (tid + u * kTkThreads);
+      if (cached && i < n) *(float4 *)(&sh.cache[i]) = v[u];
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j < n) {
+          const uint32_t key = float_key(f[j]);
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+    }
   }
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) { sh.red_lo[wave] = kmin; sh.red_hi[wave] = kmax; }
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
-  __syncthreads();
+  lds_barrier();
   kmin = sh.red_lo[0];
   kmax = sh.red_hi[0];
   for (int w2 = 1; w2 < kTkWaves; ++w2) {
@@ -151,36 +177,46 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   };
 
   // ---- 2. histogram, threshold bin ----
-  for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
-    float4 v = load4(i);
-    const float f[4] = {v.x, v.y, v.z, v.w};
+  for (int base = 0; base < n; base += kChunk) {
+    float4 v[kU];
+    DSA_SWEEP_CHUNK(base, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + j < n) atomicAdd(&sh.hist[bin_of(f[j])], 1u);
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + 4 * (tid + u * kTkThreads);
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j < n) atomicAdd(&sh.hist[bin_of(f[j])], 1u);
+    }
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) scan_from_top(sh.hist, kTkBins, k, &sh.scan_bin, &sh.scan_above);
-  __syncthreads();
+  lds_barrier();
   const int bstar = sh.scan_bin;
   int need = k - sh.scan_above;
   const int bcount = (int)sh.hist[bstar];
   const bool use_list = bcount <= kTkCand;
   if (tid == 0) sh.cand_count = 0;
-  __syncthreads();
+  lds_barrier();
 
   // ---- 3. exact threshold inside bin b* ----
   if (use_list) {
-    for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
-      float4 v = load4(i);
-      const float f[4] = {v.x, v.y, v.z, v.w};
+    for (int base = 0; base < n; base += kChunk) {
+      float4 v[kU];
+      DSA_SWEEP_CHUNK(base, v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i + j < n && bin_of(f[j]) == bstar) {
-          int slot = atomicAdd(&sh.cand_count, 1);
-          if (slot < kTkCand) sh.cand[slot] = i + j;
-        }
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + 4 * (tid + u * kTkThreads);
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i + j < n && bin_of(f[j]) == bstar) {
+            const int slot = atomicAdd(&sh.cand_count, 1);
+            if (slot < kTkCand) sh.cand[slot] = i + j;
+          }
+      }
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int ncand = min(bcount, kTkCand);
   uint32_t prefix = 0u, pmask = 0u;
@@ -189,7 +225,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < nb; i += kTkThreads) sh.hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     if (use_list) {
       for (int c = tid; c < ncand; c += kTkThreads) {
         const int pos = sh.cand[c];
@@ -197,83 +233,95 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
         if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
       }
     } else {
-      for (int i = 4 * tid; i < n; i += 4 * kTkThreads) {
-        float4 v = load4(i);
-        const float f[4] = {v.x, v.y, v.z, v.w};
+      for (int base = 0; base < n; base += kChunk) {
+        float4 v[kU];
+        DSA_SWEEP_CHUNK(base, v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t key = float_key(f[j]);
-          if (i + j < n && bin_of(f[j]) == bstar && (key & pmask) == prefix)
-            atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+        for (int u = 0; u < kU; ++u) {
+          const int i = base + 4 * (tid + u * kTkThreads);
+          const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t key = float_key(f[j]);
+            if (i + j < n && bin_of(f[j]) == bstar && (key & pmask) == prefix)
+              atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+          }
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) scan_from_top(sh.hist, nb, need, &sh.scan_bin, &sh.scan_above);
-    __syncthreads();
+    lds_barrier();
     need -= sh.scan_above;
     prefix |= (uint32_t)sh.scan_bin << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
-    __syncthreads();
+    lds_barrier();
   }
   const uint32_t tau = prefix;
   const int need_eq = need;
 
   // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
+  // Elements are visited in index order, 4096 per step (4 per thread); the
+  // loads of a whole chunk are issued before its steps.
   int gt_run = 0, eq_run = 0;
   int it = 0;
-  for (int base = 0; base < n; base += 4 * kTkThreads, ++it) {
-    const int i = base + 4 * tid;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < n) v = load4(i);
-    const float f[4] = {v.x, v.y, v.z, v.w};
-    bool gt[4], eq[4];
-    int g_lane = 0, e_lane = 0, g_tot = 0, e_tot = 0;
+  for (int base = 0; base < n; base += kChunk) {
+    float4 v[kU];
+    DSA_SWEEP_CHUNK(base, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t key = float_key(f[j]);
-      const bool valid = i + j < n;
-      gt[j] = valid && key > tau;
-      eq[j] = valid && key == tau;
-      const uint64_t bg = __ballot(gt[j]);
-      const uint64_t be = __ballot(eq[j]);
-      g_lane += lanes_below(bg);
-      e_lane += lanes_below(be);
-      g_tot += __popcll(bg);
-      e_tot += __popcll(be);
-    }
-    const int slot = it & 1;
-    if (lane == 0) { sh.cnt[slot][0][wave] = g_tot; sh.cnt[slot][1][wave] = e_tot; }
-    __syncthreads();
-    int g_wave = 0, e_wave = 0, g_blk = 0, e_blk = 0;
-    for (int w2 = 0; w2 < kTkWaves; ++w2) {
-      const int gv = sh.cnt[slot][0][w2];
-      const int ev = sh.cnt[slot][1][w2];
-      if (w2 < wave) { g_wave += gv; e_wave += ev; }
-      g_blk += gv;
-      e_blk += ev;
-    }
-    int g_before = gt_run + g_wave + g_lane;
-    int e_before = eq_run + e_wave + e_lane;
+    for (int u = 0; u < kU; ++u, ++it) {
+      if (base + 4 * u * kTkThreads >= n) break;  // uniform
+      const int i = base + 4 * (tid + u * kTkThreads);
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      bool gt[4], eq[4];
+      int g_lane = 0, e_lane = 0, g_tot = 0, e_tot = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (gt[j]) {
-        const int pos = g_before + min(e_before, need_eq);
-        if (pos < k) out[pos] = i + j;
-        ++g_before;
-      } else if (eq[j]) {
-        if (e_before < need_eq) {
-          const int pos = g_before + e_before;
-          if (pos < k) out[pos] = i + j;
-        }
-        ++e_before;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = float_key(f[j]);
+        const bool valid = i + j < n;
+        gt[j] = valid && key > tau;
+        eq[j] = valid && key == tau;
+        const uint64_t bg = __ballot(gt[j]);
+        const uint64_t be = __ballot(eq[j]);
+        g_lane += lanes_below(bg);
+        e_lane += lanes_below(be);
+        g_tot += __popcll(bg);
+        e_tot += __popcll(be);
       }
+      const int slot = it & 1;
+      if (lane == 0) { sh.cnt[slot][0][wave] = g_tot; sh.cnt[slot][1][wave] = e_tot; }
+      lds_barrier();
+      int g_wave = 0, e_wave = 0, g_blk = 0, e_blk = 0;
+      for (int w2 = 0; w2 < kTkWaves; ++w2) {
+        const int gv = sh.cnt[slot][0][w2];
+        const int ev = sh.cnt[slot][1][w2];
+        if (w2 < wave) { g_wave += gv; e_wave += ev; }
+        g_blk += gv;
+        e_blk += ev;
+      }
+      int g_before = gt_run + g_wave + g_lane;
+      int e_before = eq_run + e_wave + e_lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (gt[j]) {
+          const int pos = g_before + min(e_before, need_eq);
+          if (pos < k) out[pos] = i + j;
+          ++g_before;
+        } else if (eq[j]) {
+          if (e_before < need_eq) {
+            const int pos = g_before + e_before;
+            if (pos < k) out[pos] = i + j;
+          }
+          ++e_before;
+        }
+      }
+      gt_run += g_blk;
+      eq_run += e_blk;
     }
-    gt_run += g_blk;
-    eq_run += e_blk;
   }
   const int total = gt_run + min(eq_run, need_eq);
   for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
+#undef DSA_SWEEP_CHUNK
 }
 
 hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
