@@ -275,6 +275,8 @@ class Synth:
         wl = self.wl
         for b in range(wl.batch):
             base = int(lay.k_seq_start[b])
+            if base >= g1 or base + int(lay.k_len[b]) <= g0:
+                continue  # no key of this sequence in the range
             qrow = int(lay.q_seq_start[b + 1]) - 1
             qi = self.qi_f32(qrow, qrow + 1)[0].astype(np.float64)
             wv = self.w(qrow, qrow + 1)[0].astype(np.float64)
