@@ -104,22 +104,17 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
   const float row_scale = q_scale[t] * scale;
   float *out = scores + (int64_t)t * ld;
 
-  int s0 = s_begin + kIdxTile * wave;
-  v8i nb0 = {}, nb1 = {};
-  float nks = 0.f;
+  // Each wave walks tiles wave, wave+4, wave+8, ... of the block two at a
+  // time, with the next two tiles' loads in flight while these are computed.
   auto load_tile = [&](int s_tile, v8i &b0, v8i &b1, float &ksc) {
-    int s = min(s_tile + col, n - 1);  // clamp: stays inside the history
-    int64_t row = key_row(kd, b, s);
+    const int s = min(s_tile + col, n - 1);  // clamp: stays inside the history
+    const int64_t row = key_row(kd, b, s);
     const uint8_t *kr = k + row * 128 + 32 * half;
     b0 = *(const v8i *)(kr);
     b1 = *(const v8i *)(kr + 64);
     ksc = k_scale[row];
   };
-  if (s0 < s_end) load_tile(s0, nb0, nb1, nks);
-  for (; s0 < s_end; s0 += kIdxTile * 4) {
-    v8i b0 = nb0, b1 = nb1;
-    float ksc = nks;
-    if (s0 + kIdxTile * 4 < s_end) load_tile(s0 + kIdxTile * 4, nb0, nb1, nks);
+  auto score_tile = [&](int s_tile, const v8i &b0, const v8i &b1, float ksc) {
     float sum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -130,8 +125,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
       for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], fmaxf(acc[i], 0.f), sum);
     }
     sum += __shfl_xor(sum, 32, 64);
-    const int s = s0 + col;
+    const int s = s_tile + col;
     if (half == 0 && s < s_end) out[s] = sum * row_scale * ksc;
+  };
+  constexpr int kStep = kIdxTile * 4;  // distance between a wave's consecutive tiles
+  int s0 = s_begin + kIdxTile * wave;
+  v8i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float cs0 = 0.f, cs1 = 0.f;
+  if (s0 < s_end) load_tile(s0, c0, c1, cs0);
+  if (s0 + kStep < s_end) load_tile(s0 + kStep, c2, c3, cs1);
+  for (; s0 < s_end; s0 += 2 * kStep) {
+    v8i n0 = {}, n1 = {}, n2 = {}, n3 = {};
+    float ns0 = 0.f, ns1 = 0.f;
+    if (s0 + 2 * kStep < s_end) load_tile(s0 + 2 * kStep, n0, n1, ns0);
+    if (s0 + 3 * kStep < s_end) load_tile(s0 + 3 * kStep, n2, n3, ns1);
+    score_tile(s0, c0, c1, cs0);
+    if (s0 + kStep < s_end) score_tile(s0 + kStep, c2, c3, cs1);
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    cs0 = ns0; cs1 = ns1;
   }
 }
 

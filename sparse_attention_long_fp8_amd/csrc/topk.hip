@@ -261,63 +261,71 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   const int need_eq = need;
 
   // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
-  // Elements are visited in index order, 4096 per step (4 per thread); the
-  // loads of a whole chunk are issued before its steps.
+  // Rows are written in pieces of up to 32768 elements.  In a piece, thread i
+  // owns the contiguous run [i*R, i*R + R) (R <= 32, a multiple of 4) and keeps
+  // bitmasks of its elements above and equal to tau; one block-wide exclusive
+  // scan of the two counts gives every run its output offset, so the output
+  // comes out ascending without any per-element synchronisation.
   int gt_run = 0, eq_run = 0;
-  int it = 0;
-  for (int base = 0; base < n; base += kChunk) {
-    float4 v[kU];
-    DSA_SWEEP_CHUNK(base, v);
-#pragma unroll
-    for (int u = 0; u < kU; ++u, ++it) {
-      if (base + 4 * u * kTkThreads >= n) break;  // uniform
-      const int i = base + 4 * (tid + u * kTkThreads);
-      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      bool gt[4], eq[4];
-      int g_lane = 0, e_lane = 0, g_tot = 0, e_tot = 0;
+  for (int p0 = 0; p0 < n; p0 += kChunk) {
+    const int np = min(n - p0, kChunk);
+    const int R = ((np + kTkThreads - 1) / kTkThreads + 3) & ~3;
+    const int r0 = p0 + tid * R;
+    uint32_t gtm = 0u, eqm = 0u;
+    for (int q = 0; q < R / 4; ++q) {
+      // rotated order (q + tid) % (R/4): neighbouring lanes hit different LDS banks
+      const int qq = (q + tid) % (R / 4);
+      const int i = r0 + 4 * qq;
+      if (i >= p0 + np) continue;
+      const float4 v = cached ? *(const float4 *)(&sh.cache[i]) : *(const float4 *)(row + i);
+      const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        if (i + j >= p0 + np) break;
         const uint32_t key = float_key(f[j]);
-        const bool valid = i + j < n;
-        gt[j] = valid && key > tau;
-        eq[j] = valid && key == tau;
-        const uint64_t bg = __ballot(gt[j]);
-        const uint64_t be = __ballot(eq[j]);
-        g_lane += lanes_below(bg);
-        e_lane += lanes_below(be);
-        g_tot += __popcll(bg);
-        e_tot += __popcll(be);
+        gtm |= (uint32_t)(key > tau) << (4 * qq + j);
+        eqm |= (uint32_t)(key == tau) << (4 * qq + j);
       }
-      const int slot = it & 1;
-      if (lane == 0) { sh.cnt[slot][0][wave] = g_tot; sh.cnt[slot][1][wave] = e_tot; }
-      lds_barrier();
-      int g_wave = 0, e_wave = 0, g_blk = 0, e_blk = 0;
-      for (int w2 = 0; w2 < kTkWaves; ++w2) {
-        const int gv = sh.cnt[slot][0][w2];
-        const int ev = sh.cnt[slot][1][w2];
-        if (w2 < wave) { g_wave += gv; e_wave += ev; }
-        g_blk += gv;
-        e_blk += ev;
-      }
-      int g_before = gt_run + g_wave + g_lane;
-      int e_before = eq_run + e_wave + e_lane;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (gt[j]) {
-          const int pos = g_before + min(e_before, need_eq);
-          if (pos < k) out[pos] = i + j;
-          ++g_before;
-        } else if (eq[j]) {
-          if (e_before < need_eq) {
-            const int pos = g_before + e_before;
-            if (pos < k) out[pos] = i + j;
-          }
-          ++e_before;
-        }
-      }
-      gt_run += g_blk;
-      eq_run += e_blk;
     }
+    const int gc = __popc(gtm), ec = __popc(eqm);
+    // block-wide exclusive scan of (gc, ec): lanes, then waves
+    int gi = gc, ei = ec;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yg = __shfl_up(gi, off, 64);
+      const int ye = __shfl_up(ei, off, 64);
+      if (lane >= off) { gi += yg; ei += ye; }
+    }
+    if (lane == 63) { sh.cnt[0][0][wave] = gi; sh.cnt[0][1][wave] = ei; }
+    lds_barrier();
+    int gw = 0, ew = 0, gb = 0, eb = 0;
+    for (int w2 = 0; w2 < kTkWaves; ++w2) {
+      const int gv = sh.cnt[0][0][w2], ev = sh.cnt[0][1][w2];
+      if (w2 < wave) { gw += gv; ew += ev; }
+      gb += gv;
+      eb += ev;
+    }
+    int g_before = gt_run + gw + gi - gc;
+    int e_before = eq_run + ew + ei - ec;
+    uint32_t m = gtm | eqm;
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      const int pos_i = r0 + bit;
+      if ((gtm >> bit) & 1u) {
+        const int pos = g_before + min(e_before, need_eq);
+        if (pos < k) out[pos] = pos_i;
+        ++g_before;
+      } else {
+        if (e_before < need_eq) {
+          const int pos = g_before + e_before;
+          if (pos < k) out[pos] = pos_i;
+        }
+        ++e_before;
+      }
+    }
+    gt_run += gb;
+    eq_run += eb;
+    lds_barrier();  // sh.cnt is reused by the next piece
   }
   const int total = gt_run + min(eq_run, need_eq);
   for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
