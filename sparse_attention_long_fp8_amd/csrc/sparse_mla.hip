@@ -95,10 +95,11 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, in
 //   * rows: every slot of the range is resolved once (index -> page -> row)
 //     into LDS before the tile loop, so the loop issues no dependent loads;
 //   * gather: the 32 selected 1152-byte key rows of a tile go straight into
-//     LDS with 16-byte global->LDS loads (row pitch 1168 bytes spreads the LDS
-//     banks).  Three tile buffers keep two tiles in flight while one is
-//     computed; every wave issues exactly kLoadsPerWave loads per tile, so a
-//     per-wave vmcnt wait retires exactly the tile that is needed next;
+//     LDS with 16-byte global->LDS loads (a 1184-byte row pitch spreads the
+//     LDS banks; it measured fastest of the pitches from 1168 to 1280 bytes).
+//     Three tile buffers keep two tiles in flight while one is computed;
+//     every wave issues exactly kLoadsPerWave loads per tile, so a per-wave
+//     vmcnt wait retires exactly the tile that is needed next;
 //   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
 //       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
 //       registers for the whole launch; each LDS fragment feeds every head
@@ -123,10 +124,10 @@ constexpr int kNt = kDv / 16;                  // 32 output dim tiles
 constexpr int kBlk = 32;                       // selected tokens per tile
 constexpr int kMaxSlots = 2048;                // slots one workgroup resolves
 constexpr int kRowBytes = kD * 2;              // 1152
-constexpr int kRowSlots = kRowBytes / 16 + 1;  // 72 data chunks + 1 pad chunk
-constexpr int kRowStride = kRowSlots * 16;     // 1168-byte LDS row pitch
-constexpr int kTileSlots = kBlk * kRowSlots;   // 2336 16-byte slots
-constexpr int kTileLoads = 40;                 // wave-wide loads per tile (>= 2336/64, divisible by 8)
+constexpr int kRowSlots = kRowBytes / 16 + 2;  // 72 data chunks + 2 pad chunks
+constexpr int kRowStride = kRowSlots * 16;     // 1184-byte LDS row pitch (measured best)
+constexpr int kTileSlots = kBlk * kRowSlots;   // 2368 16-byte slots
+constexpr int kTileLoads = 40;                 // wave-wide loads per tile (>= 2368/64, divisible by 8)
 constexpr int kTileBytes = kTileLoads * 64 * 16;
 constexpr int kBufs = 3;                       // tile buffers: one computed, two in flight
 constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
@@ -186,8 +187,8 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   __syncthreads();
 
   // tile blk -> buffer buf: wave-wide load j of wave w fills LDS slots
-  // 64*(NW*j + w) .. +63; slot -> (row = slot / 73, chunk = slot % 73); chunk
-  // 72 is pitch padding and rows >= 32 tail padding (both reload chunk 0)
+  // 64*(NW*j + w) .. +63; slot -> (row = slot / 74, chunk = slot % 74); chunks
+  // 72 and 73 are pitch padding and rows >= 32 tail padding (all reload chunk 0)
   auto gather = [&](int blk, int buf) {
     const int32_t *rows = sh.rows + blk * kBlk;
 #pragma unroll 1
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       int c = slot - r * kRowSlots;
       int64_t row = r < kBlk ? rows[r] : -1;
       if (row < 0) row = row0;
-      if (c == kRowSlots - 1 || r >= kBlk) c = 0;
+      if (c >= kRowBytes / 16 || r >= kBlk) c = 0;
       lds_dma16(kv_bytes + row * kRowBytes + c * 16, &sh.tile[buf][base * 16]);
     }
   };
