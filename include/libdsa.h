@@ -111,7 +111,7 @@ typedef struct {
  * of the dequantised operands.  The [T, n, h_i] per-head products are never
  * stored.  Entries s >= n_t of each row are left untouched.
  *   dtype   DSA_FP8_E4M3 (q_idx/k_idx are bytes, q_scale/k_scale required,
- *           h_i % 16 == 0, d_i == 128) or DSA_F32 (scales must be NULL;
+ *           h_i 32, 64 or 128, d_i == 128) or DSA_F32 (scales must be NULL;
  *           h_i <= 64, d_i <= 128).
  *   q_idx   [T, h_i, d_i];  q_scale [T];  w [T, h_i] fp32
  *   k_idx   contiguous [num_rows, d_i] or paged [pages, page_size, d_i];
@@ -154,7 +154,7 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
  * by every head; the value is its first d_v entries.  An empty J gives
  * out = 0 and lse = -inf.  Indices are positions within the query's
  * sequence (as written by dsa_topk) and must be < n_t.
- *   dtype  DSA_BF16 (q, kv, out bf16; heads % 16 == 0, d_qk == 576,
+ *   dtype  DSA_BF16 (q, kv, out bf16; heads 16, 32, 64 or 128, d_qk == 576,
  *          d_v == 512) or DSA_F32 (heads <= 64, d_qk <= 128, d_v <= d_qk).
  *   q      [T, heads, d_qk];  kv contiguous [num_rows, d_qk] or paged
  *          [pages, page_size, d_qk];  indices [T, k] int32

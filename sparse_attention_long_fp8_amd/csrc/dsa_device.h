@@ -69,14 +69,13 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 
 // 16-byte global -> LDS load for a whole wave: lane i's 16 bytes land at LDS
-// byte offset lds_base + 16 * i (lds_base must be wave-uniform).  Written as
+// byte address lds_byte + 16 * i (lds_byte must be wave-uniform).  Written as
 // inline assembly so that the compiler does not treat every later LDS read as
 // possibly aliasing it (it would otherwise drain all such loads before them);
 // callers wait for completion with an explicit vmcnt wait.  M0, which carries
 // the LDS base, is saved and restored inside the block.
-__device__ __forceinline__ void lds_dma16(const void *gaddr, void *lds_dst_wave) {
-  const uint32_t base =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t *)lds_dst_wave);
+__device__ __forceinline__ void lds_dma16_at(const void *gaddr, uint32_t lds_byte) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte);
   uint32_t saved;
   __asm__ volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -87,6 +86,17 @@ __device__ __forceinline__ void lds_dma16(const void *gaddr, void *lds_dst_wave)
       : "=&s"(saved)
       : "s"(base), "v"(gaddr)
       : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// The same load with the LDS destination given as a pointer into a
+// __shared__ object.
+__device__ __forceinline__ void lds_dma16(const void *gaddr, void *lds_dst_wave) {
+  lds_dma16_at(gaddr, lds_addr(lds_dst_wave));
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.

@@ -129,7 +129,8 @@ dsa_status_t check_mla(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dty
   if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
   if (dt == DSA_BF16) {
     if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: d_qk must be 576 and d_v 512 (got %d, %d)", d_qk, d_v);
-    if (heads != 16 && heads != 64 && heads != 128) return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: heads must be 16, 64 or 128 (got %d)", heads);
+    if (heads != 16 && heads != 32 && heads != 64 && heads != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: heads must be 16, 32, 64 or 128 (got %d)", heads);
     if (!aligned(q, 16) || !aligned(kv, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "bf16 q / kv must be 16-byte aligned");
   } else if (dt == DSA_F32) {
     if (heads < 1 || d_qk < 1 || d_qk > 128 || d_v < 1 || d_v > d_qk)

@@ -29,6 +29,14 @@ __global__ void probe_bf16_16x16x32_kernel(const v8bf *a, const v8bf *b, v4f *d)
   d[l] = acc;
 }
 
+// a, b: [64][8] bf16; d: [64][16]
+__global__ void probe_bf16_32x32x16_kernel(const v8bf *a, const v8bf *b, v16f *d) {
+  const int l = threadIdx.x;
+  v16f acc = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[l], b[l], acc, 0, 0, 0);
+  d[l] = acc;
+}
+
 // src: 4096 16-bit words copied into LDS; off: per-lane byte offset (8-byte
 // aligned, < 8192 - 8, checked on the host); dst: [64][4] words read back.
 __global__ void probe_tr16_kernel(const short *src, const int *off, v4s *dst) {
@@ -66,6 +74,12 @@ int dsa_probe_fp8_32x32x64(const void *a, const void *b, float *d, hipStream_t s
 int dsa_probe_bf16_16x16x32(const void *a, const void *b, float *d, hipStream_t stream) {
   hipLaunchKernelGGL(probe_bf16_16x16x32_kernel, dim3(1), dim3(64), 0, stream, (const v8bf *)a,
                      (const v8bf *)b, (v4f *)d);
+  return (int)hipGetLastError();
+}
+
+int dsa_probe_bf16_32x32x16(const void *a, const void *b, float *d, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_bf16_32x32x16_kernel, dim3(1), dim3(64), 0, stream, (const v8bf *)a,
+                     (const v8bf *)b, (v16f *)d);
   return (int)hipGetLastError();
 }
 

@@ -253,6 +253,14 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
         s1[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ht][ks], s1[ht], 0, 0, 0);
       }
     }
+    // keep two K-steps of A fragments (4 reads) ahead of the QK MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < kKs - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * HT, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * HT, 1);
 
     // ---- online softmax (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
     bool ok[8];
@@ -319,6 +327,14 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       for (int ht = 0; ht < HT; ++ht)
         o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
     }
+    // keep three V fragments (6 transpose reads) ahead of the PV MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < kNt - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, HT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3 * HT, 0);
 
     // the next tile must have landed; the one after may stay in flight
     if (ahead) wait_vmcnt<kLoadsPerWave>(); else wait_vmcnt<0>();
@@ -357,6 +373,7 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 
 // Merge of split partials: lse = log sum_i e^{lse_i}, o = sum_i e^{lse_i - lse} o_i.
 // Block = 4 heads x 64 lanes; a lane owns 8 consecutive dims (16-byte loads).
+// The split loops are unrolled by 8 so that up to 8 loads are in flight.
 constexpr int kMaxSplits = 32;
 
 __global__ __launch_bounds__(256) void mla_combine_kernel(int heads, int nsplit,
@@ -369,17 +386,37 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int heads, int nsplit,
   const int d0 = 8 * (threadIdx.x & 63);
   if (h >= heads) return;
   const float *pl = part_lse + (int64_t)t * nsplit * heads + h;
+  const __hip_bfloat16 *po = part_o + ((int64_t)t * nsplit * heads + h) * kDv + d0;
+  const int64_t pstride = (int64_t)heads * kDv;
   float mx = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * heads]);
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u < nsplit) mx = fmaxf(mx, pl[(int64_t)(i0 + u) * heads]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int i = 0; i < nsplit; ++i) {
-    const float li = pl[(int64_t)i * heads];
-    const float wi = mx == -INFINITY ? 0.f : expf(li - mx);
-    wsum += wi;
-    const v8bf v = *(const v8bf *)(part_o + (((int64_t)t * nsplit + i) * heads + h) * kDv + d0);
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {
+    v8bf v[8];
+    float w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, (float)v[j], acc[j]);
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      w[u] = 0.f;
+      if (i < nsplit) {
+        const float li = pl[(int64_t)i * heads];
+        w[u] = mx == -INFINITY ? 0.f : expf(li - mx);
+        v[u] = *(const v8bf *)(po + i * pstride);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u < nsplit) {
+        wsum += w[u];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(w[u], (float)v[u][j], acc[j]);
+      }
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   v8bf r;
@@ -441,6 +478,11 @@ hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_querie
   switch (heads) {
     case 128:
       hipLaunchKernelGGL((mla_bf16_kernel<8, 1>), grid, dim3(512), 0, stream, bt, kd,
+                         (const __hip_bfloat16 *)q, (const __hip_bfloat16 *)kv, indices, k, per,
+                         sm_scale, (__hip_bfloat16 *)out, lse, part_o, part_lse);
+      break;
+    case 32:
+      hipLaunchKernelGGL((mla_bf16_kernel<2, 1>), grid, dim3(128), 0, stream, bt, kd,
                          (const __hip_bfloat16 *)q, (const __hip_bfloat16 *)kv, indices, k, per,
                          sm_scale, (__hip_bfloat16 *)out, lse, part_o, part_lse);
       break;

@@ -28,6 +28,9 @@ SMALL = {
     # single-head page form: H_I = 32 (smallest FP8 head count), 1/sqrt(d_I) scale, 16 MLA heads
     "prefill_h32": W("prefill_h32", 14, "prefill", 1, 200, h_i=32, top_k=50, heads=16,
                      index_scale=1.0 / np.sqrt(128)),
+    # the other MLA head counts: 64 (one workgroup per row and range) and 32
+    "decode_h64": W("decode_h64", 17, "decode", 3, 0, ctx_range=(300, 1500), top_k=192, heads=64),
+    "prefill_h32mla": W("prefill_h32mla", 18, "prefill", 1, 160, top_k=100, heads=32),
 }
 
 
@@ -93,3 +96,19 @@ def test_k_at_least_context_is_dense_attention(gpu):
     o = out.float().cpu().numpy()[:24]
     assert np.abs(o - o_d).max() / np.abs(o_d).max() <= H.ATTN_TOL_BF16
     assert np.abs(lse.cpu().numpy()[:24] - lse_d).max() <= H.LSE_TOL
+
+
+def test_wide_logit_range(gpu):
+    """Queries scaled by 32 (exact in bf16): the logits of a row spread over
+    hundreds of log2 units, so later tiles exceed a head's running reference
+    max by far more than the kernel's headroom and its rescale path runs,
+    several times per range.  Rows here have one slot range of 32 tiles."""
+    wl = W("chunk_wide", 16, "chunk", 2, 0, ctx_range=(1500, 2500), q_per_seq=64, top_k=1024)
+    c = H.GpuCase(wl, gpu)
+    idx = c.topk(c.indexer())
+    c.q = (c.q.float() * 32).to(torch.bfloat16)
+    c.q_hat = c.q_hat * 32
+    out, lse = c.mla(idx)
+    rows = list(range(0, c.T, 3))
+    worst = H.check_mla(c, idx, out, lse, rows)
+    print("[chunk_wide] worst attention error %.3g" % worst)

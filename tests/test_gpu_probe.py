@@ -20,7 +20,7 @@ PROBE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def probe(gpu):
     lib = ctypes.CDLL(PROBE)
-    for name in ("dsa_probe_fp8_32x32x64", "dsa_probe_bf16_16x16x32"):
+    for name in ("dsa_probe_fp8_32x32x64", "dsa_probe_bf16_16x16x32", "dsa_probe_bf16_32x32x16"):
         getattr(lib, name).argtypes = [ctypes.c_void_p] * 4
     lib.dsa_probe_tr16.argtypes = [ctypes.c_void_p] * 5
     return lib
@@ -115,6 +115,34 @@ def test_bf16_mfma_layout(probe, gpu):
         for i in range(4):
             D[4 * (l // 16) + i, l % 16] = d[l, i]
     ref = At.double().numpy() @ Bt.double().numpy()
+    assert np.abs(D - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_bf16_mfma_32x32x16_layout(probe, gpu):
+    """32x32x16 bf16: lane l holds A row / B column l % 32 and K elements
+    8*(l//32) .. +8; accumulator register i of lane l holds row
+    8*(i//4) + 4*(l//32) + i%4, column l % 32."""
+    rng = np.random.default_rng(2)
+    A = rng.standard_normal((32, 16)).astype(np.float32)
+    Bm = rng.standard_normal((16, 32)).astype(np.float32)
+    At = torch.from_numpy(A).to(torch.bfloat16)
+    Bt = torch.from_numpy(Bm).to(torch.bfloat16)
+    a = torch.empty((64, 8), dtype=torch.bfloat16)
+    b = torch.empty((64, 8), dtype=torch.bfloat16)
+    for l in range(64):
+        a[l] = At[l % 32, 8 * (l // 32):8 * (l // 32) + 8]
+        b[l] = Bt[8 * (l // 32):8 * (l // 32) + 8, l % 32]
+    da, db = a.to(gpu), b.to(gpu)
+    dd = torch.zeros((64, 16), dtype=torch.float32, device=gpu)
+    assert probe.dsa_probe_bf16_32x32x16(da.data_ptr(), db.data_ptr(), dd.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    d = dd.cpu().numpy()
+    D = np.full((32, 32), np.nan)
+    for l in range(64):
+        for i in range(16):
+            D[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32] = d[l, i]
+    ref = At.double().numpy() @ Bt.double().numpy()
+    assert not np.isnan(D).any()
     assert np.abs(D - ref).max() <= 1e-5 * np.abs(ref).max()
 
 
