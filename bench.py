@@ -192,20 +192,31 @@ def main():
     stream = torch.cuda.current_stream()
 
     log("warmup %d, timed %d steps, %d input copies" % (warmup, steps, copies))
+    dw.prepare_forward()
     for i in range(warmup):
+        dw.forward_prepared(i, stream)
         dw.step(i, stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # Throughput: back-to-back passes through the fused entry point, nothing
+    # else on the stream inside the timed region.
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(steps):
-        dw.step(warmup + i, stream, evs[i])
+        dw.forward_prepared(warmup + i, stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms_step = total_ms / steps
+    # Per-kernel durations: the same passes stage by stage with HIP events
+    # recorded around each stage on the launch stream (the event records add
+    # a few microseconds between stages, so this loop does not give `value`).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        dw.step(warmup + i, stream, evs[i])
+    torch.cuda.synchronize()
     stage_ms = {
         "indexer": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
         "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
