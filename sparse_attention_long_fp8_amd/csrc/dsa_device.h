@@ -93,6 +93,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// 4-byte variant: lane i's 4 bytes land at LDS byte address lds_byte + 4 * i.
+__device__ __forceinline__ void lds_dma4_at(const void *gaddr, uint32_t lds_byte) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte);
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(gaddr)
+      : "memory");
+}
+
 // The same load with the LDS destination given as a pointer into a
 // __shared__ object.
 __device__ __forceinline__ void lds_dma16(const void *gaddr, void *lds_dst_wave) {

@@ -307,6 +307,157 @@ hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_que
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// FP8 E4M3 decode form: few query rows over long key ranges.  The same MFMA
+// tiling as indexer_fp8_kernel, but keys reach the registers through LDS:
+// 128-key stages (16 KB) arrive by 16-byte global->LDS loads in which 64
+// consecutive lanes cover 1 KB of consecutive key bytes, three stages deep,
+// and their fp32 scales by 4-byte global->LDS loads.  Each wave scores one
+// 32-key tile of every stage.  The 16-byte chunks of a 128-byte key row are
+// XOR-permuted by an even mask (kswz), which keeps each lane's two operand
+// chunks adjacent and spreads the 32 rows a read instruction touches over
+// the LDS banks.  The workgroup's page bases are resolved into LDS before
+// the loop, so the loop issues no dependent global loads.
+// --------------------------------------------------------------------------
+constexpr int kDecStageKeys = 128;                 // 4 tiles of 32 keys: one per wave
+constexpr int kDecStageBytes = kDecStageKeys * 128;   // 16 KB
+constexpr int kDecStageLoads = kDecStageBytes / 1024; // 16 wave-wide key loads per stage
+constexpr int kDecStageBufs = 3;
+constexpr int kStagedKeysPerBlock = 1024;       // 8 stages
+constexpr int kStagedPages = kStagedKeysPerBlock / kPageSize;
+
+__device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) << 1; }
+
+struct IdxStagedLds {
+  uint8_t keys[kDecStageBufs][kDecStageBytes];
+  float ksc[kDecStageBufs][kDecStageKeys];
+  int64_t page_row[kStagedPages];  // flat row of key 64p of the block (contiguous: s_begin + 64p)
+};
+
+template <int MT>
+__global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
+    BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
+    const float *__restrict__ w, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld) {
+  constexpr int H = 32 * MT;
+  __shared__ IdxStagedLds sh;
+  const int t = blockIdx.y;
+  const int b = __builtin_amdgcn_readfirstlane(seq_of_row(bt, t));
+  const int n = __builtin_amdgcn_readfirstlane(candidates_of_row(bt, b, t));
+  const int s_begin = blockIdx.x * kStagedKeysPerBlock;
+  if (s_begin >= n) return;
+  const int s_end = min(n, s_begin + kStagedKeysPerBlock);
+  const int nst = (s_end - s_begin + kDecStageKeys - 1) / kDecStageKeys;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // query operand: head 32*mt + col, bytes [64*ks + 32*half, +32)
+  v8i a[MT][2];
+  const uint8_t *qt = q + (int64_t)t * H * 128;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      a[mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
+  // head weights of the accumulator rows this lane holds (rows 8r + 4*half + 0..3)
+  float wr[MT][16];
+  const float *wt = w + (int64_t)t * H;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 v = *(const float4 *)(wt + 32 * mt + 8 * r4 + 4 * half);
+      wr[mt][4 * r4 + 0] = v.x;
+      wr[mt][4 * r4 + 1] = v.y;
+      wr[mt][4 * r4 + 2] = v.z;
+      wr[mt][4 * r4 + 3] = v.w;
+    }
+  const float row_scale = q_scale[t] * scale;
+  float *out = scores + (int64_t)t * ld;
+  // page bases of the block (for the contiguous layout: rows of keys 64p)
+  if (threadIdx.x < kStagedPages) {
+    const int s = min(s_begin + kPageSize * (int)threadIdx.x, n - 1);
+    sh.page_row[threadIdx.x] = key_row(kd, b, s & ~(kPageSize - 1));
+  }
+  // The query, weight and page loads must be complete (and known complete
+  // to the compiler) before the stage loads are issued: otherwise its wait
+  // bookkeeping would later wait for them behind stage loads kept in flight.
+  __syncthreads();
+
+  const uint32_t keys0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.keys[0][0]));
+  const uint32_t ksc0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.ksc[0][0]));
+  // stage si -> buffer si % 3.  Key load j (wave + 4m) covers keys 8j .. 8j+7
+  // of the stage: lane i stores chunk i % 8 of key 8j + i/8, which holds the
+  // key's chunk (i % 8) ^ kswz(key).  Waves 0 and 1 also load the scales of
+  // keys 64*wave .. +63.  Keys past n reload key n - 1.
+  auto stage = [&](int si) __attribute__((always_inline)) {
+    const int buf = si % kDecStageBufs;
+    const int s_stage = s_begin + si * kDecStageKeys;
+#pragma unroll
+    for (int m = 0; m < kDecStageLoads / 4; ++m) {
+      const int j = wave + 4 * m;
+      const int r = 8 * j + (lane >> 3);
+      const int s = min(s_stage + r, n - 1);
+      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kDecStageBytes + 1024 * j);
+    }
+    if (wave < 2) {
+      const int s = min(s_stage + 64 * wave + lane, n - 1);
+      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      lds_dma4_at(k_scale + row, ksc0 + buf * (kDecStageKeys * 4) + 256 * wave);
+    }
+  };
+  constexpr int kLoads = kDecStageLoads / 4;  // key loads per wave per stage (+1 for waves 0, 1)
+  // wait until at most `o` of this wave's most recent stages may be in flight
+  auto wait_stages = [&](int o) __attribute__((always_inline)) {
+    if (wave < 2) {
+      if (o >= 2) wait_vmcnt<2 * (kLoads + 1)>(); else if (o == 1) wait_vmcnt<kLoads + 1>(); else wait_vmcnt<0>();
+    } else {
+      if (o >= 2) wait_vmcnt<2 * kLoads>(); else if (o == 1) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+    }
+  };
+  static_assert(kDecStageBufs <= 4, "at most three stages in flight");
+
+  // stages 0 .. B-2 in flight, then wait for stage 0
+  for (int i = 0; i < kDecStageBufs - 1 && i < nst; ++i) stage(i);
+  wait_stages(min(kDecStageBufs - 2, nst - 1));
+  lds_barrier();
+
+  // B operand reads: key r = 32*wave + col of the stage, chunks 4ks + 2half, +1
+  const int r = 32 * wave + col;
+  for (int si = 0; si < nst; ++si) {
+    const int buf = si % kDecStageBufs;
+    if (si + kDecStageBufs - 1 < nst) stage(si + kDecStageBufs - 1);
+    const uint8_t *kb = sh.keys[buf] + r * 128;
+    float sum = 0.f;
+    v8i bk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = (4 * ks + 2 * half) ^ kswz(r);
+      const v4i lo = *(const v4i *)(kb + 16 * c);
+      const v4i up = *(const v4i *)(kb + 16 * c + 16);
+      bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
+    }
+    const float ksc = sh.ksc[buf][r];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v16f acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][0], bk[0], acc, 0, 0, 0, 127, 0, 127);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][1], bk[1], acc, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], fmaxf(acc[i], 0.f), sum);
+    }
+    sum += __shfl_xor(sum, 32, 64);
+    const int s = s_begin + si * kDecStageKeys + r;
+    if (half == 0 && s < s_end) out[s] = sum * row_scale * ksc;
+    // the next stage must have landed; later ones may stay in flight
+    wait_stages(min(si + kDecStageBufs, nst) - (si + 2));
+    lds_barrier();
+  }
+}
+
 hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
                               int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,
                               const float *q_scale, const float *w, const uint8_t *k,
@@ -319,6 +470,24 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
               num_seqs);
     hipLaunchKernelGGL((indexer_fp8_tiled_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
                        q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+    return hipGetLastError();
+  }
+  if (h_i == 32 || h_i == 64 || h_i == 128) {
+    dim3 grid((max_k_len + kStagedKeysPerBlock - 1) / kStagedKeysPerBlock, num_queries);
+    switch (h_i / 32) {
+      case 1:
+        hipLaunchKernelGGL(indexer_fp8_staged_kernel<1>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                           q_scale, w, k, k_scale, scale, scores, ld);
+        break;
+      case 2:
+        hipLaunchKernelGGL(indexer_fp8_staged_kernel<2>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                           q_scale, w, k, k_scale, scale, scores, ld);
+        break;
+      default:
+        hipLaunchKernelGGL(indexer_fp8_staged_kernel<4>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                           q_scale, w, k, k_scale, scale, scores, ld);
+        break;
+    }
     return hipGetLastError();
   }
   const int keys_per_block = kIdxTile * 4 * 8;  // 4 waves x 8 tiles
