@@ -15,10 +15,11 @@
 //      (spreads typical score distributions evenly, so LDS atomics rarely
 //      collide); a wave-wide scan from the top finds the bin b* holding the
 //      k-th largest score;
-//   3. exact radix select (11/11/10-bit digits of an order-preserving uint32
-//      key) over the elements of bin b* only -- compacted into an LDS list
-//      when there are at most 1024 of them -- yields the threshold key tau
-//      and how many elements equal to tau are kept;
+//   3. the elements of bin b* only -- compacted into an LDS list when there
+//      are at most 1024 of them -- give the threshold key tau and how many
+//      elements equal to tau are kept: by direct ranking (key descending,
+//      position ascending) when the list holds at most 256, else by an exact
+//      radix select (11/11/10-bit digits of an order-preserving uint32 key);
 //   4. one ordered pass writes key > tau, plus the first `need_eq` elements
 //      equal to tau, at positions given by wave ballots and a block scan of
 //      per-wave counts: the output comes out ascending.
@@ -32,17 +33,21 @@ constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkCache = 32768;  // scores kept in LDS (128 KiB)
 constexpr int kTkBins = 2048;
 constexpr int kTkCand = 1024;
+constexpr int kTkRankMax = 256;  // bins up to this size are resolved by direct ranking
 
 struct TopkLds {
   float cache[kTkCache];
   uint32_t hist[kTkBins];
   int32_t cand[kTkCand];
+  uint32_t cand_key[kTkCand];
   uint32_t red_lo[kTkWaves];
   uint32_t red_hi[kTkWaves];
   int32_t cnt[2][2][kTkWaves];
   int32_t scan_bin;
   int32_t scan_above;
   int32_t cand_count;
+  uint32_t rank_tau;
+  int32_t rank_need_eq;
 };
 
 __device__ __forceinline__ float key_to_float(uint32_t key) {
@@ -212,7 +217,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
         for (int j = 0; j < 4; ++j)
           if (i + j < n && bin_of(f[j]) == bstar) {
             const int slot = atomicAdd(&sh.cand_count, 1);
-            if (slot < kTkCand) sh.cand[slot] = i + j;
+            if (slot < kTkCand) {
+              sh.cand[slot] = i + j;
+              sh.cand_key[slot] = float_key(f[j]);
+            }
           }
       }
     }
@@ -220,8 +228,32 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   }
   const int ncand = min(bcount, kTkCand);
   uint32_t prefix = 0u, pmask = 0u;
+  const bool by_rank = use_list && ncand <= kTkRankMax;
+  if (by_rank) {
+    // Candidate c ranks by (key descending, position ascending); the one at
+    // rank need-1 is the last kept: its key is tau, and need_eq is what is
+    // left of `need` after the candidates strictly above tau.
+    if (tid < ncand) {
+      const uint32_t ki = sh.cand_key[tid];
+      const int pi = sh.cand[tid];
+      int rank = 0, gt = 0;
+      for (int j = 0; j < ncand; ++j) {
+        const uint32_t kj = sh.cand_key[j];
+        const int pj = sh.cand[j];
+        gt += kj > ki;
+        rank += (kj > ki) | ((kj == ki) & (pj < pi));
+      }
+      if (rank == need - 1) {
+        sh.rank_tau = ki;
+        sh.rank_need_eq = need - gt;
+      }
+    }
+    lds_barrier();
+    prefix = sh.rank_tau;
+    need = sh.rank_need_eq;
+  }
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < (by_rank ? 0 : 3); ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < nb; i += kTkThreads) sh.hist[i] = 0;

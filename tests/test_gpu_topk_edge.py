@@ -1,0 +1,61 @@
+"""Top-k on crafted score rows, bit-exact against the oracle's selection:
+heavy ties (small bins resolved by ranking, large ones by radix digits), a
+constant row (the whole row is one bin, past the candidate list), signed
+zeros, all-negative rows, rows longer than the LDS row cache, and rows
+shorter than k.  Each row is its own sequence, so n_t = k_len[t]; entries
+past n_t are NaN and must never be read."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from sparse_attention_long_fp8_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(kind, rng):
+    if kind == "ties_small_bins":
+        return [rng.integers(0, 4000, 5000).astype(np.float32) for _ in range(6)], 300
+    if kind == "ties_few_values":
+        return [rng.integers(0, 3, 20000).astype(np.float32) for _ in range(3)], 2048
+    if kind == "constant":
+        return [np.full(4000, 1.5, np.float32), np.full(3000, -2.0, np.float32)], 100
+    if kind == "signed_zero":
+        r = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), 3000)
+        return [r, np.where(rng.random(3000) < 0.5, np.float32(-0.0), np.float32(0.0))], 64
+    if kind == "all_negative":
+        return [-rng.random(9000).astype(np.float32) - 1.0 for _ in range(2)], 512
+    if kind == "long_rows":
+        return [rng.integers(0, 1000, 70000).astype(np.float32), rng.standard_normal(100000).astype(np.float32)], 2048
+    if kind == "short_rows":
+        return [rng.standard_normal(n).astype(np.float32) for n in (1, 10, 63, 64, 65)], 64
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["ties_small_bins", "ties_few_values", "constant", "signed_zero",
+                                  "all_negative", "long_rows", "short_rows"])
+def test_topk_crafted_rows(kind, gpu):
+    print("\n[topk-edge] %s" % kind, flush=True)
+    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    rows, k = _rows(kind, rng)
+    T = len(rows)
+    ns = [len(r) for r in rows]
+    ld = (max(ns) + 3) // 4 * 4
+    scores = np.full((T, ld), np.nan, np.float32)
+    for t, r in enumerate(rows):
+        scores[t, :len(r)] = r
+    q_seq_start = torch.arange(T + 1, dtype=torch.int32, device=gpu)
+    k_len = torch.tensor(ns, dtype=torch.int32, device=gpu)
+    batch = B.make_batch(q_seq_start, k_len, T, T, 1, max(ns))
+    d_scores = torch.from_numpy(scores).to(gpu)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=gpu)
+    B.dsa_topk(batch, d_scores, ld, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().astype(np.int64)
+    for t, r in enumerate(rows):
+        want = O.topk_indices(r.astype(np.float64), k)
+        assert np.array_equal(got[t], want), "%s row %d (n=%d): top-k differs" % (kind, t, len(r))
