@@ -46,105 +46,22 @@ __global__ __launch_bounds__(kIdxF32Threads) void indexer_f32_kernel(
 }
 
 // --------------------------------------------------------------------------
-// FP8 E4M3 path, d_i = 128, h_i = 32 * MT.
+// FP8 E4M3 path, d_i = 128, h_i = 32 * MT: the MFMA tiling both FP8 kernels
+// below share.
 //
 // Per query row, the heads are the M dimension of a 32x32x64 FP8 MFMA and
 // 32 keys its N dimension: a wave multiplies the row's [h_i x 128] query
-// block (kept in registers for the whole launch) by a [128 x 32] key tile
-// read straight from HBM, two K-steps per 32 heads.  Lane l supplies
-// operand row/column l % 32 and the 32-byte K-slice 32 * (l / 32) of each
-// 64-wide K-step, identically for both operands, so the products pair
-// matching d.  The accumulator lane holds column l % 32 (its key) and rows
-// 8 * (i / 4) + 4 * (l / 32) + i % 4 (its heads); ReLU and the head weight
-// are applied there, and the two half-waves' partial sums are added with one
-// cross-lane swap.  Every key byte is read once per query row.
+// block (kept in registers) by a [128 x 32] key tile, two K-steps per 32
+// heads.  Lane l supplies operand row/column l % 32 and the 32-byte K-slice
+// 32 * (l / 32) of each 64-wide K-step, identically for both operands, so the
+// products pair matching d.  The accumulator lane holds column l % 32 (its
+// key) and rows 8 * (i / 4) + 4 * (l / 32) + i % 4 (its heads); ReLU and the
+// head weight are applied there, and the two half-waves' partial sums are
+// added with one cross-lane swap.  Key tiles reach the registers through LDS,
+// staged by 16-byte global->LDS loads.
 // --------------------------------------------------------------------------
 constexpr int kIdxThreads = 256;  // 4 waves
-constexpr int kIdxTile = 32;      // keys per MFMA tile
 
-template <int MT>
-__global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(
-    BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
-    const float *__restrict__ w, const uint8_t *__restrict__ k,
-    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld,
-    int keys_per_block) {
-  constexpr int H = 32 * MT;
-  const int t = blockIdx.y;
-  const int b = seq_of_row(bt, t);
-  const int n = candidates_of_row(bt, b, t);
-  const int s_begin = blockIdx.x * keys_per_block;
-  if (s_begin >= n) return;
-  const int s_end = min(n, s_begin + keys_per_block);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-
-  // query operand: head 32*mt + col, bytes [64*ks + 32*half, +32)
-  v8i a[MT][2];
-  const uint8_t *qt = q + (int64_t)t * H * 128;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      a[mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
-  // head weights of the accumulator rows this lane holds (rows 8r + 4*half + 0..3)
-  float wr[MT][16];
-  const float *wt = w + (int64_t)t * H;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 v = *(const float4 *)(wt + 32 * mt + 8 * r4 + 4 * half);
-      wr[mt][4 * r4 + 0] = v.x;
-      wr[mt][4 * r4 + 1] = v.y;
-      wr[mt][4 * r4 + 2] = v.z;
-      wr[mt][4 * r4 + 3] = v.w;
-    }
-  const float row_scale = q_scale[t] * scale;
-  float *out = scores + (int64_t)t * ld;
-
-  // Each wave walks tiles wave, wave+4, wave+8, ... of the block two at a
-  // time, with the next two tiles' loads in flight while these are computed.
-  auto load_tile = [&](int s_tile, v8i &b0, v8i &b1, float &ksc) {
-    const int s = min(s_tile + col, n - 1);  // clamp: stays inside the history
-    const int64_t row = key_row(kd, b, s);
-    const uint8_t *kr = k + row * 128 + 32 * half;
-    b0 = *(const v8i *)(kr);
-    b1 = *(const v8i *)(kr + 64);
-    ksc = k_scale[row];
-  };
-  auto score_tile = [&](int s_tile, const v8i &b0, const v8i &b1, float ksc) {
-    float sum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      v16f acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][0], b0, acc, 0, 0, 0, 127, 0, 127);
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][1], b1, acc, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], fmaxf(acc[i], 0.f), sum);
-    }
-    sum += __shfl_xor(sum, 32, 64);
-    const int s = s_tile + col;
-    if (half == 0 && s < s_end) out[s] = sum * row_scale * ksc;
-  };
-  constexpr int kStep = kIdxTile * 4;  // distance between a wave's consecutive tiles
-  int s0 = s_begin + kIdxTile * wave;
-  v8i c0 = {}, c1 = {}, c2 = {}, c3 = {};
-  float cs0 = 0.f, cs1 = 0.f;
-  if (s0 < s_end) load_tile(s0, c0, c1, cs0);
-  if (s0 + kStep < s_end) load_tile(s0 + kStep, c2, c3, cs1);
-  for (; s0 < s_end; s0 += 2 * kStep) {
-    v8i n0 = {}, n1 = {}, n2 = {}, n3 = {};
-    float ns0 = 0.f, ns1 = 0.f;
-    if (s0 + 2 * kStep < s_end) load_tile(s0 + 2 * kStep, n0, n1, ns0);
-    if (s0 + 3 * kStep < s_end) load_tile(s0 + 3 * kStep, n2, n3, ns1);
-    score_tile(s0, c0, c1, cs0);
-    if (s0 + kStep < s_end) score_tile(s0 + kStep, c2, c3, cs1);
-    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
-    cs0 = ns0; cs1 = ns1;
-  }
-}
 
 // --------------------------------------------------------------------------
 // FP8 E4M3 path for many query rows per sequence (prefill, chunked prefill).
@@ -308,11 +225,10 @@ hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_que
 }
 
 // --------------------------------------------------------------------------
-// FP8 E4M3 decode form: few query rows over long key ranges.  The same MFMA
-// tiling as indexer_fp8_kernel, but keys reach the registers through LDS:
-// 128-key stages (16 KB) arrive by 16-byte global->LDS loads in which 64
-// consecutive lanes cover 1 KB of consecutive key bytes, three stages deep,
-// and their fp32 scales by 4-byte global->LDS loads.  Each wave scores one
+// FP8 E4M3 decode form: few query rows over long key ranges.  128-key stages
+// (16 KB) arrive by 16-byte global->LDS loads in which 64 consecutive lanes
+// cover 1 KB of consecutive key bytes, three stages deep, and their fp32
+// scales by 4-byte global->LDS loads.  Each wave scores one
 // 32-key tile of every stage.  The 16-byte chunks of a 128-byte key row are
 // XOR-permuted by an even mask (kswz), which keeps each lane's two operand
 // chunks adjacent and spreads the 32 rows a read instruction touches over
@@ -472,38 +388,19 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
                        q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
     return hipGetLastError();
   }
-  if (h_i == 32 || h_i == 64 || h_i == 128) {
-    dim3 grid((max_k_len + kStagedKeysPerBlock - 1) / kStagedKeysPerBlock, num_queries);
-    switch (h_i / 32) {
-      case 1:
-        hipLaunchKernelGGL(indexer_fp8_staged_kernel<1>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                           q_scale, w, k, k_scale, scale, scores, ld);
-        break;
-      case 2:
-        hipLaunchKernelGGL(indexer_fp8_staged_kernel<2>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                           q_scale, w, k, k_scale, scale, scores, ld);
-        break;
-      default:
-        hipLaunchKernelGGL(indexer_fp8_staged_kernel<4>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                           q_scale, w, k, k_scale, scale, scores, ld);
-        break;
-    }
-    return hipGetLastError();
-  }
-  const int keys_per_block = kIdxTile * 4 * 8;  // 4 waves x 8 tiles
-  dim3 grid((max_k_len + keys_per_block - 1) / keys_per_block, num_queries);
-  switch (h_i / 32) {
-    case 1:
-      hipLaunchKernelGGL(indexer_fp8_kernel<1>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+  dim3 grid((max_k_len + kStagedKeysPerBlock - 1) / kStagedKeysPerBlock, num_queries);
+  switch (h_i) {
+    case 32:
+      hipLaunchKernelGGL(indexer_fp8_staged_kernel<1>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q, q_scale,
+                         w, k, k_scale, scale, scores, ld);
       break;
-    case 2:
-      hipLaunchKernelGGL(indexer_fp8_kernel<2>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+    case 64:
+      hipLaunchKernelGGL(indexer_fp8_staged_kernel<2>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q, q_scale,
+                         w, k, k_scale, scale, scores, ld);
       break;
-    case 4:
-      hipLaunchKernelGGL(indexer_fp8_kernel<4>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                         q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+    case 128:
+      hipLaunchKernelGGL(indexer_fp8_staged_kernel<4>, grid, dim3(kIdxThreads), 0, stream, bt, kd, q, q_scale,
+                         w, k, k_scale, scale, scores, ld);
       break;
     default:
       return hipErrorInvalidValue;
