@@ -97,9 +97,10 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, in
 //   * gather: the 32 selected 1152-byte key rows of a tile go straight into
 //     LDS with 16-byte global->LDS loads (a 1184-byte row pitch spreads the
 //     LDS banks; it measured fastest of the pitches from 1168 to 1280 bytes).
-//     Three tile buffers keep two tiles in flight while one is computed;
-//     every wave issues exactly kLoadsPerWave loads per tile, so a per-wave
-//     vmcnt wait retires exactly the tile that is needed next;
+//     A tile is exactly 37 wave-wide 1 KB loads.  Four tile buffers keep
+//     three tiles in flight while one is computed; a wave issues the same
+//     number of loads for every tile, so a per-wave vmcnt wait retires
+//     exactly the tile that is needed next;
 //   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
 //       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
 //       registers for the whole launch; each LDS fragment feeds every head
@@ -127,11 +128,11 @@ constexpr int kRowBytes = kD * 2;              // 1152
 constexpr int kRowSlots = kRowBytes / 16 + 2;  // 72 data chunks + 2 pad chunks
 constexpr int kRowStride = kRowSlots * 16;     // 1184-byte LDS row pitch (measured best)
 constexpr int kTileSlots = kBlk * kRowSlots;   // 2368 16-byte slots
-constexpr int kTileLoads = 40;                 // wave-wide loads per tile (>= 2368/64, divisible by 8)
+constexpr int kTileLoads = kTileSlots / 64;    // 37 wave-wide 1 KB loads per tile
 constexpr int kTileBytes = kTileLoads * 64 * 16;
-constexpr int kBufs = 3;                       // tile buffers: one computed, two in flight
+constexpr int kBufs = 4;                       // tile buffers: one computed, three in flight
 constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
-static_assert(kTileLoads * 64 >= kTileSlots, "tile loads cover the tile");
+static_assert(kTileLoads * 64 == kTileSlots, "tile loads cover the tile exactly");
 
 struct MlaLds {
   uint8_t tile[kBufs][kTileBytes];
@@ -150,8 +151,9 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   constexpr int HW = 16 * HT;  // heads per wave
   constexpr int H = HW * NW;
   constexpr int NT = NW * 64;
-  constexpr int kLoadsPerWave = kTileLoads / NW;
-  static_assert(kTileLoads % NW == 0, "every wave issues the same number of tile loads");
+  // waves below kTileLoads % NW issue one load more per tile than the others
+  constexpr int kLHi = (kTileLoads + NW - 1) / NW;
+  constexpr int kLLo = kTileLoads / NW;
   __shared__ MlaLds sh;
 
   const int t = blockIdx.x;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   const int nsplit = gridDim.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;    // lane group
   const int n16 = lane & 15;  // column within a 16-wide tile
   const int b = seq_of_row(bt, t);
@@ -188,19 +190,33 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 
   // tile blk -> buffer buf: wave-wide load j of wave w fills LDS slots
   // 64*(NW*j + w) .. +63; slot -> (row = slot / 74, chunk = slot % 74); chunks
-  // 72 and 73 are pitch padding and rows >= 32 tail padding (all reload chunk 0)
-  auto gather = [&](int blk, int buf) {
+  // 72 and 73 are pitch padding (they reload chunk 0 of the row)
+  const bool hi = wave < kTileLoads % NW;
+  auto gather = [&](int blk, int buf) __attribute__((always_inline)) {
     const int32_t *rows = sh.rows + blk * kBlk;
+    const int nl = hi ? kLHi : kLLo;
 #pragma unroll 1
-    for (int j = 0; j < kLoadsPerWave; ++j) {
+    for (int j = 0; j < nl; ++j) {
       const int base = 64 * (NW * j + wave);
       const int slot = base + lane;
       const int r = slot / kRowSlots;
       int c = slot - r * kRowSlots;
-      int64_t row = r < kBlk ? rows[r] : -1;
+      int64_t row = rows[r];
       if (row < 0) row = row0;
-      if (c >= kRowBytes / 16 || r >= kBlk) c = 0;
-      lds_dma16(kv_bytes + row * kRowBytes + c * 16, &sh.tile[buf][base * 16]);
+      if (c >= kRowBytes / 16) c = 0;
+      lds_dma16_at(kv_bytes + row * kRowBytes + c * 16, lds_addr(&sh.tile[buf][0]) + base * 16);
+    }
+  };
+  // wait until at most `n` tiles of this wave's loads are still in flight
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+    if (hi) {
+      if (n >= 2) wait_vmcnt<(2 * kLHi < 63 ? 2 * kLHi : 63)>();
+      else if (n == 1) wait_vmcnt<(kLHi < 63 ? kLHi : 63)>();
+      else wait_vmcnt<0>();
+    } else {
+      if (n >= 2) wait_vmcnt<(2 * kLLo < 63 ? 2 * kLLo : 63)>();
+      else if (n == 1) wait_vmcnt<(kLLo < 63 ? kLLo : 63)>();
+      else wait_vmcnt<0>();
     }
   };
 
@@ -219,19 +235,13 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   // before the tile loop: otherwise its wait bookkeeping re-waits for them in
   // every iteration, draining the tile loads kept in flight.
   wait_vmcnt<0>();
-  if (nblk > 0) gather(0, 0);
-  if (nblk > 1) {
-    gather(1, 1);
-    wait_vmcnt<kLoadsPerWave>();  // tile 0 (and the query operand) landed
-  } else {
-    wait_vmcnt<0>();
-  }
+  for (int p = 0; p < kBufs - 1 && p < nblk; ++p) gather(p, p);
+  wait_tiles(min(nblk, kBufs - 1) - 1);  // tile 0 landed
   lds_barrier();
 
   for (int blk = 0; blk < nblk; ++blk) {
     const int buf = blk % kBufs;
-    const bool ahead = blk + 2 < nblk;
-    if (ahead) gather(blk + 2, (blk + 2) % kBufs);
+    if (blk + kBufs - 1 < nblk) gather(blk + kBufs - 1, (blk + kBufs - 1) % kBufs);
     const uint8_t *tile = sh.tile[buf];
     const int32_t *rows = sh.rows + blk * kBlk;
 
@@ -336,8 +346,8 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3 * HT, 0);
 
-    // the next tile must have landed; the one after may stay in flight
-    if (ahead) wait_vmcnt<kLoadsPerWave>(); else wait_vmcnt<0>();
+    // the next tile must have landed; the ones after it may stay in flight
+    wait_tiles(min(nblk - 1, blk + kBufs - 1) - (blk + 1));
     lds_barrier();
   }
 
