@@ -8,8 +8,8 @@
 // order).  Ties go to the lowest position, so the result is unique and the
 // kernel is deterministic.
 //
-// One 1024-thread workgroup owns a row and keeps it in LDS when it fits
-// (up to 32768 scores).  Selection is exact:
+// One 1024-thread workgroup owns a row and keeps its first 32768 scores (the
+// whole row when it fits) in LDS.  Selection is exact:
 //   1. min / max of the row (while caching it);
 //   2. histogram of a monotone linear binning of the values into 2048 bins
 //      (spreads typical score distributions evenly, so LDS atomics rarely
@@ -21,8 +21,8 @@
 //      position ascending) when the list holds at most 256, else by an exact
 //      radix select (11/11/10-bit digits of an order-preserving uint32 key);
 //   4. one ordered pass writes key > tau, plus the first `need_eq` elements
-//      equal to tau, at positions given by wave ballots and a block scan of
-//      per-wave counts: the output comes out ascending.
+//      equal to tau, at positions given by block scans of per-thread (row in
+//      LDS) or per-wave (longer rows) counts: the output comes out ascending.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -137,10 +137,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     return;
   }
   const float *row = scores + (int64_t)t * ld;
+  // The first sweep keeps the row's first chunk (all of it when n <= 32768)
+  // in LDS; every later sweep reads that chunk from there.
+  static_assert(kChunk == kTkCache, "the cached part of a row is its first sweep chunk");
   const bool cached = n <= kTkCache;
-  // every sweep after the first reads the LDS copy when the row fits
-#define DSA_SWEEP_CHUNK(base, v)              \
-  if (cached) load_chunk(sh.cache, base, n, v); \
+#define DSA_SWEEP_CHUNK(base, v)                   \
+  if (base == 0) load_chunk(sh.cache, base, n, v); \
   else load_chunk(row, base, n, v);
 
   // ---- 1. cache the row, min / max key ----
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = base + 4 * (tid + u * kTkThreads);
-      if (cached && i < n) *(float4 *)(&sh.cache[i]) = v[u];
+      if (base == 0 && i < n) *(float4 *)(&sh.cache[i]) = v[u];
       const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     if (use_list) {
       for (int c = tid; c < ncand; c += kTkThreads) {
         const int pos = sh.cand[c];
-        const uint32_t key = float_key(cached ? sh.cache[pos] : row[pos]);
+        const uint32_t key = float_key(pos < kTkCache ? sh.cache[pos] : row[pos]);
         if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
       }
     } else {
@@ -293,71 +295,165 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   const int need_eq = need;
 
   // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
-  // Rows are written in pieces of up to 32768 elements.  In a piece, thread i
-  // owns the contiguous run [i*R, i*R + R) (R <= 32, a multiple of 4) and keeps
-  // bitmasks of its elements above and equal to tau; one block-wide exclusive
-  // scan of the two counts gives every run its output offset, so the output
-  // comes out ascending without any per-element synchronisation.
   int gt_run = 0, eq_run = 0;
-  for (int p0 = 0; p0 < n; p0 += kChunk) {
-    const int np = min(n - p0, kChunk);
-    const int R = ((np + kTkThreads - 1) / kTkThreads + 3) & ~3;
-    const int r0 = p0 + tid * R;
-    uint32_t gtm = 0u, eqm = 0u;
-    for (int q = 0; q < R / 4; ++q) {
-      // rotated order (q + tid) % (R/4): neighbouring lanes hit different LDS banks
-      const int qq = (q + tid) % (R / 4);
-      const int i = r0 + 4 * qq;
-      if (i >= p0 + np) continue;
-      const float4 v = cached ? *(const float4 *)(&sh.cache[i]) : *(const float4 *)(row + i);
-      const float f[4] = {v.x, v.y, v.z, v.w};
+  if (cached) {
+    // The row is in LDS.  Thread i owns the contiguous run [i*R, i*R + R)
+    // (R <= 32, a multiple of 4) and keeps bitmasks of its elements above and
+    // equal to tau; one block-wide exclusive scan of the two counts gives
+    // every run its output offset, so the output comes out ascending without
+    // any per-element synchronisation.
+    for (int p0 = 0; p0 < n; p0 += kChunk) {
+      const int np = min(n - p0, kChunk);
+      const int R = ((np + kTkThreads - 1) / kTkThreads + 3) & ~3;
+      const int r0 = p0 + tid * R;
+      uint32_t gtm = 0u, eqm = 0u;
+      for (int q = 0; q < R / 4; ++q) {
+        // rotated order (q + tid) % (R/4): neighbouring lanes hit different LDS banks
+        const int qq = (q + tid) % (R / 4);
+        const int i = r0 + 4 * qq;
+        if (i >= p0 + np) continue;
+        const float4 v = *(const float4 *)(&sh.cache[i]);
+        const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (i + j >= p0 + np) break;
-        const uint32_t key = float_key(f[j]);
-        gtm |= (uint32_t)(key > tau) << (4 * qq + j);
-        eqm |= (uint32_t)(key == tau) << (4 * qq + j);
-      }
-    }
-    const int gc = __popc(gtm), ec = __popc(eqm);
-    // block-wide exclusive scan of (gc, ec): lanes, then waves
-    int gi = gc, ei = ec;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int yg = __shfl_up(gi, off, 64);
-      const int ye = __shfl_up(ei, off, 64);
-      if (lane >= off) { gi += yg; ei += ye; }
-    }
-    if (lane == 63) { sh.cnt[0][0][wave] = gi; sh.cnt[0][1][wave] = ei; }
-    lds_barrier();
-    int gw = 0, ew = 0, gb = 0, eb = 0;
-    for (int w2 = 0; w2 < kTkWaves; ++w2) {
-      const int gv = sh.cnt[0][0][w2], ev = sh.cnt[0][1][w2];
-      if (w2 < wave) { gw += gv; ew += ev; }
-      gb += gv;
-      eb += ev;
-    }
-    int g_before = gt_run + gw + gi - gc;
-    int e_before = eq_run + ew + ei - ec;
-    uint32_t m = gtm | eqm;
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      m &= m - 1;
-      const int pos_i = r0 + bit;
-      if ((gtm >> bit) & 1u) {
-        const int pos = g_before + min(e_before, need_eq);
-        if (pos < k) out[pos] = pos_i;
-        ++g_before;
-      } else {
-        if (e_before < need_eq) {
-          const int pos = g_before + e_before;
-          if (pos < k) out[pos] = pos_i;
+        for (int j = 0; j < 4; ++j) {
+          if (i + j >= p0 + np) break;
+          const uint32_t key = float_key(f[j]);
+          gtm |= (uint32_t)(key > tau) << (4 * qq + j);
+          eqm |= (uint32_t)(key == tau) << (4 * qq + j);
         }
-        ++e_before;
       }
+      const int gc = __popc(gtm), ec = __popc(eqm);
+      // block-wide exclusive scan of (gc, ec): lanes, then waves
+      int gi = gc, ei = ec;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int yg = __shfl_up(gi, off, 64);
+        const int ye = __shfl_up(ei, off, 64);
+        if (lane >= off) { gi += yg; ei += ye; }
+      }
+      if (lane == 63) { sh.cnt[0][0][wave] = gi; sh.cnt[0][1][wave] = ei; }
+      lds_barrier();
+      int gw = 0, ew = 0, gb = 0, eb = 0;
+      for (int w2 = 0; w2 < kTkWaves; ++w2) {
+        const int gv = sh.cnt[0][0][w2], ev = sh.cnt[0][1][w2];
+        if (w2 < wave) { gw += gv; ew += ev; }
+        gb += gv;
+        eb += ev;
+      }
+      int g_before = gt_run + gw + gi - gc;
+      int e_before = eq_run + ew + ei - ec;
+      uint32_t m = gtm | eqm;
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        const int pos_i = r0 + bit;
+        if ((gtm >> bit) & 1u) {
+          const int pos = g_before + min(e_before, need_eq);
+          if (pos < k) out[pos] = pos_i;
+          ++g_before;
+        } else {
+          if (e_before < need_eq) {
+            const int pos = g_before + e_before;
+            if (pos < k) out[pos] = pos_i;
+          }
+          ++e_before;
+        }
+      }
+      gt_run += gb;
+      eq_run += eb;
+      lds_barrier();  // sh.cnt is reused by the next piece
     }
-    gt_run += gb;
-    eq_run += eb;
-    lds_barrier();  // sh.cnt is reused by the next piece
+  } else {
+    // The row is read in pieces of 32768 elements (the first from LDS), each
+    // cut into one 2048-element segment per wave; lane l holds elements
+    // 256*u + 4*l + j (u < 8, j < 4) of its wave's segment, so every wave-wide
+    // load is one contiguous 1 KB and all eight are in flight together.  The
+    // waves' counts above and equal to tau, exchanged once through LDS, give
+    // each wave its output offsets; inside a wave, ballots of the per-lane
+    // counts give each lane its offsets, run by run.
+    constexpr int kSeg = kChunk / kTkWaves;  // 2048
+    int par = 0;
+    for (int p0 = 0; p0 < n; p0 += kChunk, par ^= 1) {
+      const int s0 = p0 + wave * kSeg + 4 * lane;
+      float4 v[kU];
+      if (p0 == 0) {  // the cached first piece
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = s0 + 256 * u;
+          v[u] = i < n ? *(const float4 *)(&sh.cache[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = s0 + 256 * u;
+          v[u] = i < n ? *(const float4 *)(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      uint32_t gtm = 0u, eqm = 0u;  // bit 4u+j: element s0 + 256u + j
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool in = s0 + 256 * u + j < n;
+          const uint32_t key = float_key(f[j]);
+          gtm |= (uint32_t)(in && key > tau) << (4 * u + j);
+          eqm |= (uint32_t)(in && key == tau) << (4 * u + j);
+        }
+      }
+      int gw = __popc(gtm), ew = __popc(eqm);
+      for (int off = 32; off > 0; off >>= 1) {
+        gw += __shfl_xor(gw, off, 64);
+        ew += __shfl_xor(ew, off, 64);
+      }
+      // the counts are double-buffered over pieces: the barrier of the next
+      // piece separates these reads from the next writes of the same buffer
+      if (lane == 0) { sh.cnt[par][0][wave] = gw; sh.cnt[par][1][wave] = ew; }
+      lds_barrier();
+      int g_before = gt_run, e_before = eq_run, gb = 0, eb = 0;
+      for (int w2 = 0; w2 < kTkWaves; ++w2) {
+        const int gv = sh.cnt[par][0][w2], ev = sh.cnt[par][1][w2];
+        if (w2 < wave) { g_before += gv; e_before += ev; }
+        gb += gv;
+        eb += ev;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t gn = (gtm >> (4 * u)) & 15u, en = (eqm >> (4 * u)) & 15u;
+        const int cg = __popc(gn), ce = __popc(en);
+        // exclusive lane prefix and wave total of cg, ce (0..4: three bit planes)
+        int pg = 0, pe = 0, tg = 0, te = 0;
+#pragma unroll
+        for (int bit = 0; bit < 3; ++bit) {
+          const uint64_t bg = __ballot((cg >> bit) & 1), be = __ballot((ce >> bit) & 1);
+          pg += lanes_below(bg) << bit;
+          pe += lanes_below(be) << bit;
+          tg += __popcll(bg) << bit;
+          te += __popcll(be) << bit;
+        }
+        int gpos = g_before + pg, epos = e_before + pe;
+        uint32_t m = gn | en;
+        while (m) {
+          const int j = __ffs(m) - 1;
+          m &= m - 1;
+          const int pos_i = s0 + 256 * u + j;
+          if ((gn >> j) & 1u) {
+            const int pos = gpos + min(epos, need_eq);
+            if (pos < k) out[pos] = pos_i;
+            ++gpos;
+          } else {
+            if (epos < need_eq) {
+              const int pos = gpos + epos;
+              if (pos < k) out[pos] = pos_i;
+            }
+            ++epos;
+          }
+        }
+        g_before += tg;
+        e_before += te;
+      }
+      gt_run += gb;
+      eq_run += eb;
+    }
   }
   const int total = gt_run + min(eq_run, need_eq);
   for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
