@@ -82,7 +82,15 @@ def stage_work(wl, lay):
 
 
 KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
-KERNEL_NAMES = {"indexer": "indexer_fp8_kernel", "topk": "topk_kernel", "mla": "mla_bf16_kernel"}
+def kernel_name(stage, wl, lay):
+    """The kernel a stage's time is attributed to (the launcher's choice)."""
+    if stage == "indexer":
+        if not wl.fp8:
+            return "indexer_f32_kernel"
+        return "indexer_fp8_tiled_kernel" if lay.max_q_per_seq >= 8 and wl.h_i == 64 else "indexer_fp8_staged_kernel"
+    if stage == "topk":
+        return "topk_kernel"
+    return "mla_bf16_kernel" if wl.fp8 else "mla_f32_kernel"
 
 
 def source_hash(stage):
@@ -237,7 +245,7 @@ def main():
                                   "unit": "TFLOP/s", "frac": ach / wk["peak_flops"]}
         tr = traffic_of(st_name, wl.name)
         rooflines[st_name]["traffic"] = tr
-        rooflines[st_name]["kernel"] = KERNEL_NAMES[st_name]
+        rooflines[st_name]["kernel"] = kernel_name(st_name, wl, lay)
         rooflines[st_name]["us"] = stage_ms[st_name] * 1e3
     dominant = max(stage_ms, key=stage_ms.get)
     result = {

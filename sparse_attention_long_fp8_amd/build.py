@@ -25,6 +25,11 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "libdsa.cpp"]
+
+# Per-source flags.  The FP8 indexer reads every MFMA result with VALU code
+# (ReLU, head weights); keeping the accumulators in ordinary VGPRs saves one
+# AGPR->VGPR move per element.
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 PROBE_SOURCES = ["probe.hip"]
 
 LIB_PATH = os.path.join(PKG, "libdsa.so")
@@ -52,8 +57,9 @@ def _check_no_scratch(src, verbose):
     memory.  A spilled or dynamically indexed register array (>= 128 bytes
     per lane here) costs far more than any of these kernels' arithmetic; a
     few spilled loop-invariant dwords outside the hot loops do not."""
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
-                              "-Rpass-analysis=kernel-resource-usage"]
+    cmd = [HIPCC] + COMMON + SOURCE_FLAGS.get(src, []) + [
+        "-x", "hip", "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+        "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     fn, bad = None, []
     for line in r.stderr.splitlines():
@@ -71,7 +77,7 @@ def _compile(src, verbose):
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    _run([HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    _run([HIPCC] + COMMON + SOURCE_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
     if src.endswith(".hip"):
         _check_no_scratch(src, verbose)
     return obj

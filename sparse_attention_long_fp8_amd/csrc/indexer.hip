@@ -62,37 +62,63 @@ __global__ __launch_bounds__(kIdxF32Threads) void indexer_f32_kernel(
 // --------------------------------------------------------------------------
 constexpr int kIdxThreads = 256;  // 4 waves
 
+// max(x, 0) in one integer max on the bit pattern: a float with the sign bit
+// set (negative, -0, or a negative-signed NaN) is a negative int and becomes
+// +0; everything else passes unchanged.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 
 // --------------------------------------------------------------------------
 // FP8 E4M3 path for many query rows per sequence (prefill, chunked prefill).
 //
 // A workgroup of 4 waves takes QT = 4*QW consecutive query rows of one
-// sequence (wave w owns rows QW*w .. QW*w+QW-1) and a chunk of that
-// sequence's keys.  Keys are staged 64 at a time into LDS with 16-byte
-// global->LDS loads (each wave-wide load covers 8 whole key rows, 1 KiB of
-// contiguous memory), double buffered, so every key byte crosses HBM/L2 once
-// per workgroup instead of once per query row.  Chunk c of key r is stored at
-// slot 8r + (c ^ ((r >> 1) & 7)): the XOR spreads the 32 rows a B-fragment
-// read touches over distinct LDS banks.  Per wave and 32-key subtile, the
-// staged fragments feed QW rows x MT head tiles of 32x32x64 MFMAs; ReLU,
-// head weights and the head sum happen on the accumulators as in the
-// single-row kernel.  Keys at or beyond a row's candidate count are computed
-// (the tile is shared) but not stored; subtiles entirely beyond it are skipped.
+// sequence (wave w owns rows QW*w .. QW*w+QW-1) and a block of up to 2048 of
+// that sequence's keys, so every key byte crosses L2 once per workgroup
+// rather than once per query row.  The block arrives in 128-key stages
+// (16 KB of keys, laid out as in the decode form below, plus their fp32
+// scales) by global->LDS loads, four buffers deep: three stages are in
+// flight while one is scored.  Per wave and 32-key subtile the staged
+// fragments feed QW rows x MT head tiles of 32x32x64 MFMAs; ReLU, head
+// weights and the head sum happen on the accumulators as in the decode form.
+// Keys at or beyond a row's candidate count are computed (the tile is shared)
+// but not stored; subtiles beyond every row's count are skipped.
+//
+// Wait accounting.  Vector-memory stores share the load counter and may
+// retire out of order with respect to loads, so each wait allows only as many
+// outstanding operations as there are stage loads issued after the stage it
+// needs (stores can then only make it wait longer).  The scores of a stage
+// are stored at the start of the next one, so by the time of that stage's
+// wait they have normally retired and do not eat into the allowance.  Every
+// row's scores go out through a buffer store whose range ends at the row's
+// last stored key: out-of-range lanes are dropped by the hardware, which
+// keeps the store count of every stage the same.
 // --------------------------------------------------------------------------
-constexpr int kStageKeys = 64;
-constexpr int kStageBytes = kStageKeys * 128;
+constexpr int kTStageKeys = 128;
+constexpr int kTStageBytes = kTStageKeys * 128;     // 16 KB
+constexpr int kTStageLoads = kTStageBytes / 1024;   // 16 wave-wide key loads per stage
+constexpr int kTBufs = 4;
+constexpr int kTKeysPerBlock = 2048;
+constexpr int kTPages = kTKeysPerBlock / kPageSize;
 
-typedef __attribute__((address_space(3))) void lds_void_i;
+__device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) << 1; }
+
+struct IdxTiledLds {
+  uint8_t keys[kTBufs][kTStageBytes];
+  float ksc[kTBufs][kTStageKeys];
+  int64_t page_row[kTPages];  // flat row of key 64p of the block
+};
 
 template <int MT, int QW>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
     BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k,
-    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld,
-    int keys_per_block) {
+    const float *__restrict__ k_scale, float scale, float *__restrict__ scores, int64_t ld) {
   constexpr int H = 32 * MT;
   constexpr int QT = 4 * QW;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+  constexpr int kSub = kTStageKeys / 32;  // subtiles per stage
+  __shared__ IdxTiledLds sh;
 
   const int b = blockIdx.z;
   const int q0 = bt.q_seq_start[b];
@@ -102,27 +128,28 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
   const int kl = bt.k_len[b];
   const int first_pos = kl - nq;  // position of the sequence's query 0
   const int n_max = first_pos + min(nq, g0 + QT);  // candidates of the group's last row
-  const int s_begin = blockIdx.x * keys_per_block;
+  const int s_begin = blockIdx.x * kTKeysPerBlock;
   if (s_begin >= n_max) return;
-  const int s_end = min(n_max, s_begin + keys_per_block);
+  const int s_end = min(n_max, s_begin + kTKeysPerBlock);
+  const int nst = (s_end - s_begin + kTStageKeys - 1) / kTStageKeys;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // rows of this wave: query index i within the sequence, candidates n
-  int row_t[QW], row_n[QW];
+  // rows of this wave: candidates n, query operand, head weights, output range
+  int row_n[QW];
   v8i a[QW][MT][2];
   float wr[QW][MT][16];
   float row_scale[QW];
+  __amdgpu_buffer_rsrc_t orow[QW];
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     const int i = g0 + QW * wave + j;
     const bool live = i < nq;
     const int t = q0 + (live ? i : nq - 1);
-    row_t[j] = t;
     row_n[j] = live ? first_pos + i + 1 : 0;
     const uint8_t *qt = q + (int64_t)t * H * 128;
 #pragma unroll
@@ -142,73 +169,128 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
         wr[j][mt][4 * r4 + 3] = v.w;
       }
     row_scale[j] = q_scale[t] * scale;
+    // stored keys of the row: [s_begin, min(n, s_end)); byte offsets from key s_begin
+    const int lim = max(min(row_n[j], s_end) - s_begin, 0);
+    orow[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)t * ld + s_begin, 0, 4 * lim, 0x00020000);
   }
+  if (tid < kTPages) {
+    const int s = min(s_begin + kPageSize * tid, n_max - 1);
+    sh.page_row[tid] = key_row(kd, b, s & ~(kPageSize - 1));
+  }
+  // The query, weight and page loads must be complete (and known complete
+  // to the compiler) before the stage loads are issued: otherwise its wait
+  // bookkeeping would later wait for them behind stage loads kept in flight.
+  // (The barrier alone does not wait for global loads.)
+  wait_vmcnt<0>();
+  __syncthreads();
 
-  // stage keys [s0, s0 + 64): wave w issues wave-wide loads w and w + 4, each
-  // filling 64 slots = 8 key rows
-  auto stage_keys = [&](int s0, int buf) {
+  const uint32_t keys0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.keys[0][0]));
+  const uint32_t ksc0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.ksc[0][0]));
+  // stage si -> buffer si % 4.  Key load j (wave + 4m) covers keys 8j .. 8j+7
+  // of the stage: lane i stores chunk i % 8 of key 8j + i/8, which holds the
+  // key's chunk (i % 8) ^ kswz(key).  Waves 0 and 1 also load the scales of
+  // keys 64*wave .. +63.  Keys past n_max reload key n_max - 1.
+  auto stage = [&](int si) __attribute__((always_inline)) {
+    const int buf = si % kTBufs;
+    const int s_stage = s_begin + si * kTStageKeys;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = wave + 4 * jj;
+    for (int m = 0; m < kTStageLoads / 4; ++m) {
+      const int j = wave + 4 * m;
       const int r = 8 * j + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int s = min(s0 + r, n_max - 1);
-      const int64_t row = key_row(kd, b, s);
-      __builtin_amdgcn_global_load_lds((const void *)(k + row * 128 + 16 * c),
-                                       (lds_void_i *)(&stage[buf][64 * 16 * j]), 16, 0, 0);
+      const int s = min(s_stage + r, n_max - 1);
+      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kTStageBytes + 1024 * j);
+    }
+    if (wave < 2) {
+      const int s = min(s_stage + 64 * wave + lane, n_max - 1);
+      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      lds_dma4_at(k_scale + row, ksc0 + buf * (kTStageKeys * 4) + 256 * wave);
     }
   };
+  constexpr int kLoads = kTStageLoads / 4;  // key loads per wave per stage (+1 for waves 0, 1)
+  // wait until at most `o` stage load groups issued after the needed stage
+  // may be in flight
+  auto wait_stages = [&](int o) __attribute__((always_inline)) {
+    if (wave < 2) {
+      if (o >= 2) wait_vmcnt<2 * (kLoads + 1)>(); else if (o == 1) wait_vmcnt<kLoads + 1>(); else wait_vmcnt<0>();
+    } else {
+      if (o >= 2) wait_vmcnt<2 * kLoads>(); else if (o == 1) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+    }
+  };
+  static_assert(kTBufs == 4, "the waits above cover at most two later stages");
 
-  const int nstage = (s_end - s_begin + kStageKeys - 1) / kStageKeys;
-  stage_keys(s_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int s0 = s_begin + st * kStageKeys;
-    const int buf = st & 1;
-    if (st + 1 < nstage) stage_keys(s0 + kStageKeys, buf ^ 1);
-    const uint8_t *sb = stage[buf];
+  // scores of the previous stage, stored at the start of the next one
+  float held[QW][kSub];
+  int held_off = 0;  // byte offset of the held stage's key 0 from key s_begin
+  auto store_held = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int sk0 = s0 + 32 * sub;
+    for (int j = 0; j < QW; ++j)
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[j][sub]), orow[j],
+                                              half ? 0x7FFFFFF0 : held_off + 4 * (32 * sub + col), 0, 0);
+  };
+
+  // stages 0 .. 2 in flight, then wait for stage 0
+  for (int i = 0; i < kTBufs - 1 && i < nst; ++i) stage(i);
+  wait_stages(min(kTBufs - 2, nst - 1));
+  lds_barrier();
+
+  for (int si = 0; si < nst; ++si) {
+    const int buf = si % kTBufs;
+    if (si > 0) store_held();
+    if (si + kTBufs - 1 < nst) stage(si + kTBufs - 1);
+    const int s_stage = s_begin + si * kTStageKeys;
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int sk0 = s_stage + 32 * sub;
       bool any = false;
 #pragma unroll
       for (int j = 0; j < QW; ++j) any |= sk0 < row_n[j];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) held[j][sub] = 0.f;
       if (!any) continue;  // uniform over the wave
       // B fragments of keys sk0 .. sk0+31: lane key r = 32*sub + col,
       // K-step ks holds chunks 4ks + 2*half and 4ks + 2*half + 1
       const int r = 32 * sub + col;
-      const int swz = (r >> 1) & 7;
-      v8i bf[2];
+      const uint8_t *kb = sh.keys[buf] + r * 128;
+      v8i bk[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 4 * ks + 2 * half;
-        const v4i lo = *(const v4i *)(sb + 16 * (8 * r + (c0 ^ swz)));
-        const v4i hi = *(const v4i *)(sb + 16 * (8 * r + ((c0 + 1) ^ swz)));
-        bf[ks] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int c = (4 * ks + 2 * half) ^ kswz(r);
+        const v4i lo = *(const v4i *)(kb + 16 * c);
+        const v4i up = *(const v4i *)(kb + 16 * c + 16);
+        bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
       }
-      const int s = sk0 + col;
-      const float ksc = k_scale[key_row(kd, b, min(s, n_max - 1))];
+      const float ksc = sh.ksc[buf][r];
+      // every row is scored (a row past its candidate count only on the
+      // diagonal; those scores fall outside its store range), so that the
+      // MFMAs of one row can overlap the ReLU/weight sum of another
+      v16f acc[QW][MT];
 #pragma unroll
-      for (int j = 0; j < QW; ++j) {
-        if (sk0 >= row_n[j]) continue;  // uniform over the wave
-        float sum = 0.f;
+      for (int j = 0; j < QW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          v16f acc = {};
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][0], bf[0], acc, 0, 0, 0, 127, 0, 127);
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][1], bf[1], acc, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], fmaxf(acc[i], 0.f), sum);
+          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][0], bk[0], v16f{}, 0, 0, 0, 127, 0, 127);
+          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][1], bk[1], acc[j][mt], 0, 0, 0, 127, 0, 127);
         }
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], relu(acc[j][mt][i]), sum);
         sum += __shfl_xor(sum, 32, 64);
-        if (half == 0 && s < row_n[j] && s < s_end)
-          scores[(int64_t)row_t[j] * ld + s] = sum * row_scale[j] * ksc;
+        held[j][sub] = sum * row_scale[j] * ksc;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    held_off = 4 * (si * kTStageKeys);
+    // the next stage must have landed; later ones may stay in flight
+    wait_stages(min(si + kTBufs - 1, nst - 1) - (si + 1));
+    lds_barrier();
   }
+  store_held();
 }
 
 // --------------------------------------------------------------------------
@@ -241,8 +323,6 @@ constexpr int kDecStageLoads = kDecStageBytes / 1024; // 16 wave-wide key loads 
 constexpr int kDecStageBufs = 3;
 constexpr int kStagedKeysPerBlock = 1024;       // 8 stages
 constexpr int kStagedPages = kStagedKeysPerBlock / kPageSize;
-
-__device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) << 1; }
 
 struct IdxStagedLds {
   uint8_t keys[kDecStageBufs][kDecStageBytes];
@@ -300,6 +380,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
   // The query, weight and page loads must be complete (and known complete
   // to the compiler) before the stage loads are issued: otherwise its wait
   // bookkeeping would later wait for them behind stage loads kept in flight.
+  // (The barrier alone does not wait for global loads.)
+  wait_vmcnt<0>();
   __syncthreads();
 
   const uint32_t keys0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.keys[0][0]));
@@ -363,7 +445,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][0], bk[0], acc, 0, 0, 0, 127, 0, 127);
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt][1], bk[1], acc, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], fmaxf(acc[i], 0.f), sum);
+      for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], relu(acc[i]), sum);
     }
     sum += __shfl_xor(sum, 32, 64);
     const int s = s_begin + si * kDecStageKeys + r;
@@ -381,11 +463,10 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
                               hipStream_t stream) {
   if (max_q_per_seq >= 8 && h_i == 64) {
     constexpr int QW = 2;
-    const int keys_per_block = 2048;
-    dim3 grid((max_k_len + keys_per_block - 1) / keys_per_block, (max_q_per_seq + 4 * QW - 1) / (4 * QW),
+    dim3 grid((max_k_len + kTKeysPerBlock - 1) / kTKeysPerBlock, (max_q_per_seq + 4 * QW - 1) / (4 * QW),
               num_seqs);
     hipLaunchKernelGGL((indexer_fp8_tiled_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                       q_scale, w, k, k_scale, scale, scores, ld, keys_per_block);
+                       q_scale, w, k, k_scale, scale, scores, ld);
     return hipGetLastError();
   }
   dim3 grid((max_k_len + kStagedKeysPerBlock - 1) / kStagedKeysPerBlock, num_queries);
