@@ -69,6 +69,13 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// x of this lane plus x of the lane 32 away, by a swap of the two half-waves'
+// registers (no LDS traffic, unlike a shuffle): both halves get low + high.
+__device__ __forceinline__ float add_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 
 // --------------------------------------------------------------------------
 // FP8 E4M3 path for many query rows per sequence (prefill, chunked prefill).
@@ -102,7 +109,13 @@ constexpr int kTBufs = 4;
 constexpr int kTKeysPerBlock = 2048;
 constexpr int kTPages = kTKeysPerBlock / kPageSize;
 
-__device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) << 1; }
+// Chunk permutation of a staged 128-byte key row: LDS chunk position p of key
+// r holds the key's chunk p ^ kswz(r).  A B-fragment read takes one 16-byte
+// chunk from each of 16 consecutive keys per 256-byte bank window; keys of
+// one parity share a 128-byte half of that window, and (r >> 1) & 7 gives the
+// eight keys of each parity eight distinct chunk positions, so the 16 reads
+// cover all banks.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 
 struct IdxTiledLds {
   uint8_t keys[kTBufs][kTStageBytes];
@@ -257,9 +270,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
       v8i bk[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int c = (4 * ks + 2 * half) ^ kswz(r);
-        const v4i lo = *(const v4i *)(kb + 16 * c);
-        const v4i up = *(const v4i *)(kb + 16 * c + 16);
+        const int c = 4 * ks + 2 * half;
+        const v4i lo = *(const v4i *)(kb + 16 * (c ^ kswz(r)));
+        const v4i up = *(const v4i *)(kb + 16 * ((c + 1) ^ kswz(r)));
         bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
       }
       const float ksc = sh.ksc[buf][r];
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], relu(acc[j][mt][i]), sum);
-        sum += __shfl_xor(sum, 32, 64);
+        sum = add_halves(sum);
         held[j][sub] = sum * row_scale[j] * ksc;
       }
     }
@@ -312,9 +325,8 @@ hipError_t launch_indexer_f32(const BatchDev &bt, const KeysDev &kd, int num_que
 // cover 1 KB of consecutive key bytes, three stages deep, and their fp32
 // scales by 4-byte global->LDS loads.  Each wave scores one
 // 32-key tile of every stage.  The 16-byte chunks of a 128-byte key row are
-// XOR-permuted by an even mask (kswz), which keeps each lane's two operand
-// chunks adjacent and spreads the 32 rows a read instruction touches over
-// the LDS banks.  The workgroup's page bases are resolved into LDS before
+// XOR-permuted (kswz), which spreads the 32 rows a read instruction touches
+// over the LDS banks.  The workgroup's page bases are resolved into LDS before
 // the loop, so the loop issues no dependent global loads.
 // --------------------------------------------------------------------------
 constexpr int kDecStageKeys = 128;                 // 4 tiles of 32 keys: one per wave
@@ -433,9 +445,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
     v8i bk[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int c = (4 * ks + 2 * half) ^ kswz(r);
-      const v4i lo = *(const v4i *)(kb + 16 * c);
-      const v4i up = *(const v4i *)(kb + 16 * c + 16);
+      const int c = 4 * ks + 2 * half;
+      const v4i lo = *(const v4i *)(kb + 16 * (c ^ kswz(r)));
+      const v4i up = *(const v4i *)(kb + 16 * ((c + 1) ^ kswz(r)));
       bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
     }
     const float ksc = sh.ksc[buf][r];
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum = fmaf(wr[mt][i], relu(acc[i]), sum);
     }
-    sum += __shfl_xor(sum, 32, 64);
+    sum = add_halves(sum);
     const int s = s_begin + si * kDecStageKeys + r;
     if (half == 0 && s < s_end) out[s] = sum * row_scale * ksc;
     // the next stage must have landed; later ones may stay in flight
