@@ -398,33 +398,39 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int heads, int nsplit,
   const float *pl = part_lse + (int64_t)t * nsplit * heads + h;
   const __hip_bfloat16 *po = part_o + ((int64_t)t * nsplit * heads + h) * kDv + d0;
   const int64_t pstride = (int64_t)heads * kDv;
-  float mx = -INFINITY;
-  for (int i0 = 0; i0 < nsplit; i0 += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (i0 + u < nsplit) mx = fmaxf(mx, pl[(int64_t)(i0 + u) * heads]);
-  }
+  // the partials' loads go out together with their lse loads (one memory
+  // round trip per group of 8 splits); the weights follow from the group max
+  float mx = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   for (int i0 = 0; i0 < nsplit; i0 += 8) {
     v8bf v[8];
-    float w[8];
+    float li[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u;
-      w[u] = 0.f;
+      li[u] = -INFINITY;
       if (i < nsplit) {
-        const float li = pl[(int64_t)i * heads];
-        w[u] = mx == -INFINITY ? 0.f : expf(li - mx);
+        li[u] = pl[(int64_t)i * heads];
         v[u] = *(const v8bf *)(po + i * pstride);
       }
     }
+    float gm = mx;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, li[u]);
+    if (gm == -INFINITY) continue;  // nothing selected so far
+    // rescale what was accumulated against the previous max
+    const float c = mx == -INFINITY ? 0.f : expf(mx - gm);
+    wsum *= c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= c;
+    mx = gm;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (i0 + u < nsplit) {
-        wsum += w[u];
+      if (i0 + u < nsplit && li[u] != -INFINITY) {
+        const float w = expf(li[u] - mx);
+        wsum += w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(w[u], (float)v[u][j], acc[j]);
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, (float)v[u][j], acc[j]);
       }
     }
   }
