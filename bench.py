@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel on MIB mebibytes (counter calibration) and exit")
+    ap.add_argument("--op", default="forward", choices=["forward", "cache_append"],
+                    help="forward: the hot path (default); cache_append: the decode-step cache append "
+                         "(--workload append_prefill_16k | append_decode_64)")
     return ap.parse_args()
 
 
@@ -170,6 +173,100 @@ def calibrate_copy(mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
+# --------------------------------------------------------------------------
+APPEND_WORKLOADS = {
+    # one new token for each of 64 paged sequences of 4096 cached tokens
+    "append_decode_64": {"tokens": 64, "paged": True, "seqs": 64, "k_len": 4096},
+    # a 16384-token prefill chunk written into one contiguous history
+    "append_prefill_16k": {"tokens": 16384, "paged": False, "seqs": 1, "k_len": 16384},
+}
+
+
+def bench_cache_append(args):
+    """Times dsa_cache_append and prints one JSON line (its own metric)."""
+    import torch
+    from oracle import cache_oracle  # CPU baseline leg only
+    from sparse_attention_long_fp8_amd import binding as B
+
+    name = args.workload if args.workload in APPEND_WORKLOADS else "append_prefill_16k"
+    cfg = APPEND_WORKLOADS[name]
+    d_i, d_c, ps = 128, 576, 64
+    N, S, L = cfg["tokens"], cfg["seqs"], cfg["k_len"]
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 20
+    copies = args.copies if args.copies is not None else 4
+    dev = torch.device("cuda:0")
+    B.lib()
+    rng = np.random.default_rng(21)
+    if cfg["paged"]:
+        pages = S * (L // ps)
+        table = rng.permutation(pages).astype(np.int32).reshape(S, L // ps)
+        tab_d = torch.from_numpy(table).to(dev)
+        layout = B.make_paged_layout(tab_d, L // ps, pages, ps)
+        layout_np = {"paged": True, "page_table": table, "page_size": ps}
+        rows_shape = (pages, ps)
+        seq = np.arange(S, dtype=np.int32)
+        pos = np.full(S, L - 1, np.int32)
+    else:
+        ks = np.array([0, L], np.int64)
+        ks_d = torch.from_numpy(ks).to(dev)
+        layout = B.make_contiguous_layout(ks_d, L)
+        layout_np = {"k_seq_start": ks}
+        rows_shape = (L,)
+        seq = np.zeros(N, np.int32)
+        pos = np.arange(N, dtype=np.int32)
+    k_pool = torch.zeros(rows_shape + (d_i,), dtype=torch.uint8, device=dev)
+    s_pool = torch.zeros(rows_shape, dtype=torch.float32, device=dev)
+    l_pool = torch.zeros(rows_shape + (d_c,), dtype=torch.int16, device=dev)
+    seq_d, pos_d = torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev)
+    k_new = [torch.randn(N, d_i, device=dev) for _ in range(copies)]
+    lat = [torch.randint(-16384, 16384, (N, d_c), dtype=torch.int16, device=dev) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        B.dsa_cache_append(layout, N, seq_d, pos_d, d_i, k_new[i % copies], k_pool, s_pool, d_c,
+                           lat[i % copies], l_pool, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_token = d_i * 4 + d_c * 2 + 8 + d_i + 4 + d_c * 2  # reads (key, latent, seq, pos) + writes
+    achieved = N * per_token / (ms / 1e3)
+    result = {
+        "metric": "tokens/sec appended to the caches (E4M3 indexer key + scale, bf16 latent row)",
+        "value": N / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32->e4m3+bf16", "data": "synthetic",
+        "config": {"workload": name, "tokens": N, "d_i": d_i, "d_c": d_c, "paged": cfg["paged"],
+                   "input_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None, "kernel": "cache_append_kernel",
+                     "bytes_per_token": per_token},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        m = min(N, 2048)
+        kn = k_new[0][:m].cpu().numpy()
+        ln = lat[0][:m].cpu().numpy().view(np.uint16)
+        kp = np.zeros(rows_shape + (d_i,), np.uint8)
+        sp = np.zeros(rows_shape, np.float32)
+        lp = np.zeros(rows_shape + (d_c,), np.uint16)
+        t0 = time.perf_counter()
+        cache_oracle.cache_append(layout_np, seq[:m], pos[:m], kn, ln, kp, sp, lp)
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": m / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": "first %d of %d tokens of %s; float32/float64 numpy, one thread of "
+                                            "Python per token; %.2f s" % (m, N, name, el)}
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -179,6 +276,9 @@ def main():
     import torch
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.op == "cache_append":
+        bench_cache_append(args)
         return
     from sparse_attention_long_fp8_amd import binding as B
     from sparse_attention_long_fp8_amd import synth

@@ -211,6 +211,42 @@ dsa_status_t dsa_forward(const dsa_forward_args_t *args, void *workspace,
 dsa_status_t dsa_forward_workspace_size(const dsa_forward_args_t *args, size_t *bytes);
 
 /* ------------------------------------------------------------------------
+ * Decode-step cache append.  Writes the cache entries of `num_tokens` new
+ * tokens into the pools the stages above read: the FP8 indexer key with its
+ * per-token scale ([G] Stage 1, item 1: the indexer's states are FP8) and
+ * the latent row the sparse stage gathers ([G] Stage 2).  "Sparse Attention
+ * Architectures for Long-Context Inference: Evolution and Engineering
+ * Practices", section 6, names this per-step cache update.  Token i belongs
+ * to sequence seq[i] at logical position pos[i]; its row is found with the
+ * rules of dsa_kv_layout_t (paged: page_table[seq * stride + pos / 64],
+ * slot pos % 64; contiguous: k_seq_start[seq] + pos).  In fp32:
+ *
+ *   amax = max_d |k_new[i,d]|;   sc = amax / 448  (1 when amax == 0)
+ *   k_pool[row, d]   = E4M3 code of clamp(k_new[i,d] / sc, -448, 448),
+ *                      rounded to nearest, ties to even (sign kept for zero)
+ *   k_scale_pool[row] = sc
+ *   latent_pool[row, :] = latent_new[i, :]    (bf16, copied bit for bit)
+ *
+ * Only the addressed rows are written.  Two tokens of one call must not
+ * address the same row (they would race).
+ *   num_tokens >= 0;  seq, pos [num_tokens] int32
+ *   d_i: multiple of 4, 4..512;  k_new [num_tokens, d_i] fp32 (16-byte
+ *        aligned);  k_pool contiguous [num_rows, d_i] or paged
+ *        [pages, page_size, d_i] E4M3 bytes (4-byte aligned);
+ *        k_scale_pool [num_rows] or [pages, page_size] fp32
+ *   d_c: multiple of 8 up to 4096, or 0 for keys only (the latent pointers
+ *        are then ignored);  latent_new [num_tokens, d_c] and latent_pool
+ *        [num_rows, d_c] / [pages, page_size, d_c] bf16, 16-byte aligned
+ *   Device-side preconditions (not checked): seq[i] is a sequence of the
+ *   layout, pos[i] maps to an assigned page (paged) or a row < num_rows.
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_cache_append(const dsa_kv_layout_t *layout, int32_t num_tokens,
+                              const int32_t *seq, const int32_t *pos, int32_t d_i,
+                              const float *k_new, void *k_pool, float *k_scale_pool,
+                              int32_t d_c, const void *latent_new, void *latent_pool,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ---------------------------------------------------------------------- */
 const char *dsa_status_string(dsa_status_t status);   /* static string */

@@ -64,6 +64,8 @@ _SIGS = {
                                       ctypes.POINTER(c_size)],
     "dsa_forward": [ctypes.POINTER(dsa_forward_args_t), c_ptr, c_size, c_ptr],
     "dsa_forward_workspace_size": [ctypes.POINTER(dsa_forward_args_t), ctypes.POINTER(c_size)],
+    "dsa_cache_append": [ctypes.POINTER(dsa_kv_layout_t), c_i32, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
+                         c_i32, c_ptr, c_ptr, c_ptr],
     "dsa_status_string": [c_i32],
     "dsa_last_error": [],
     "dsa_abi_version": [],
@@ -205,6 +207,16 @@ def dsa_forward(args, workspace=None, workspace_bytes=0, stream=None, check=True
                            _stream(stream))
     if check:
         _check(st, "dsa_forward")
+    return st
+
+
+def dsa_cache_append(layout, num_tokens, seq, pos, d_i, k_new, k_pool, k_scale_pool, d_c=0, latent_new=None,
+                     latent_pool=None, stream=None, check=True):
+    st = lib().dsa_cache_append(ctypes.byref(layout), int(num_tokens), _p(seq), _p(pos), int(d_i), _p(k_new),
+                                _p(k_pool), _p(k_scale_pool), int(d_c), _p(latent_new), _p(latent_pool),
+                                _stream(stream))
+    if check:
+        _check(st, "dsa_cache_append")
     return st
 
 

@@ -24,7 +24,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
-LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "libdsa.cpp"]
+LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "libdsa.cpp"]
 
 # Per-source flags.  The FP8 indexer reads every MFMA result with VALU code
 # (ReLU, head weights); keeping the accumulators in ordinary VGPRs saves one

@@ -40,4 +40,9 @@ hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_querie
                            float sm_scale, void *out, float *lse, void *workspace,
                            hipStream_t stream);
 
+hipError_t launch_cache_append(const KeysDev &kd, int num_tokens, const int32_t *seq,
+                               const int32_t *pos, int d_i, const float *k_new, void *k_pool,
+                               float *k_scale_pool, int d_c, const void *latent_new,
+                               void *latent_pool, hipStream_t stream);
+
 }  // namespace dsa

@@ -306,4 +306,39 @@ dsa_status_t dsa_forward(const dsa_forward_args_t *a, void *workspace, size_t wo
                             a->top_k, a->sm_scale, a->out, a->lse, mla_ws_ptr, mla_bytes, stream);
 }
 
+dsa_status_t dsa_cache_append(const dsa_kv_layout_t *ly, int32_t num_tokens, const int32_t *seq, const int32_t *pos,
+                              int32_t d_i, const float *k_new, void *k_pool, float *k_scale_pool, int32_t d_c,
+                              const void *latent_new, void *latent_pool, hipStream_t stream) {
+  if (!ly) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: layout is NULL");
+  if (ly->paged != 0 && ly->paged != 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: paged must be 0 or 1");
+  if (ly->num_rows < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: num_rows must be >= 1");
+  if (ly->paged) {
+    if (!ly->page_table) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: page_table is NULL");
+    if (ly->page_size != dsa::kPageSize)
+      return fail(DSA_ERR_UNSUPPORTED, "cache append: page_size %d (only %d is implemented)", ly->page_size, dsa::kPageSize);
+    if (ly->page_table_stride < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: page_table_stride must be >= 1");
+  } else if (!ly->k_seq_start) {
+    return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: k_seq_start is NULL");
+  }
+  if (num_tokens < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: num_tokens must be >= 0");
+  if (d_i < 4 || d_i > 512 || d_i % 4 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "cache append: d_i must be a multiple of 4 in [4, 512] (got %d)", d_i);
+  if (d_c < 0 || d_c > 4096 || d_c % 8 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "cache append: d_c must be 0 or a multiple of 8 up to 4096 (got %d)", d_c);
+  if (num_tokens > 0) {
+    if (!seq || !pos || !k_new || !k_pool || !k_scale_pool)
+      return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: seq, pos, k_new, k_pool and k_scale_pool must be non-NULL");
+    if (!aligned(k_new, 16) || !aligned(k_pool, 4) || !aligned(k_scale_pool, 4))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: k_new must be 16-byte and k_pool / k_scale_pool 4-byte aligned");
+    if (d_c > 0) {
+      if (!latent_new || !latent_pool) return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: latent_new / latent_pool is NULL");
+      if (!aligned(latent_new, 16) || !aligned(latent_pool, 16))
+        return fail(DSA_ERR_INVALID_ARGUMENT, "cache append: latent_new / latent_pool must be 16-byte aligned");
+    }
+  }
+  return hip_status(dsa::launch_cache_append(to_dev(ly), num_tokens, seq, pos, d_i, k_new, k_pool, k_scale_pool, d_c,
+                                             d_c > 0 ? latent_new : nullptr, d_c > 0 ? latent_pool : nullptr, stream),
+                    "cache append launch");
+}
+
 }  // extern "C"

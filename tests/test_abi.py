@@ -21,7 +21,7 @@ def _layout(rows=8):
 def test_exports_match_header():
     lib = B.lib()
     names = B.header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
 
@@ -140,3 +140,27 @@ def test_struct_offsets_match_a_c_compiler(tmp_path):
     assert sizes == [ctypes.sizeof(B.dsa_batch_t), ctypes.sizeof(B.dsa_kv_layout_t),
                      ctypes.sizeof(B.dsa_forward_args_t)]
     assert [int(x) for x in out[3:]] == [getattr(B.dsa_forward_args_t, f).offset for f in fields]
+
+
+def test_cache_append_validation():
+    lib = B.lib()
+    ly = _layout()
+    assert lib.dsa_cache_append(None, 1, 0x10, 0x20, 128, 0x100, 0x200, 0x300, 576, 0x400, 0x500, None) \
+        == B.DSA_ERR_INVALID_ARGUMENT
+    # d_i must be a multiple of 4, d_c a multiple of 8
+    assert B.dsa_cache_append(ly, 1, 0x10, 0x20, 126, 0x100, 0x200, 0x300, check=False) == B.DSA_ERR_UNSUPPORTED
+    assert B.dsa_cache_append(ly, 1, 0x10, 0x20, 128, 0x100, 0x200, 0x300, 20, 0x400, 0x500,
+                              check=False) == B.DSA_ERR_UNSUPPORTED
+    # alignment of the fp32 keys and of the latent rows
+    assert B.dsa_cache_append(ly, 1, 0x10, 0x20, 128, 0x104, 0x200, 0x300, check=False) \
+        == B.DSA_ERR_INVALID_ARGUMENT
+    assert B.dsa_cache_append(ly, 1, 0x10, 0x20, 128, 0x100, 0x200, 0x300, 576, 0x408, 0x500,
+                              check=False) == B.DSA_ERR_INVALID_ARGUMENT
+    # a missing latent pool with d_c > 0
+    assert B.dsa_cache_append(ly, 1, 0x10, 0x20, 128, 0x100, 0x200, 0x300, 576, 0x400, None,
+                              check=False) == B.DSA_ERR_INVALID_ARGUMENT
+    # paged pools: only 64-token pages
+    paged = B.dsa_kv_layout_t(1, None, 0x3000, 4, 32, 8)
+    assert B.dsa_cache_append(paged, 1, 0x10, 0x20, 128, 0x100, 0x200, 0x300, check=False) == B.DSA_ERR_UNSUPPORTED
+    # no tokens: nothing to check beyond the shapes, nothing launched
+    assert B.dsa_cache_append(ly, 0, None, None, 128, None, None, None, check=False) == B.DSA_OK
