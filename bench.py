@@ -84,9 +84,11 @@ def stage_work(wl, lay):
     }
 
 
-KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip"}
+KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "mla": "sparse_mla.hip", "indexer_topk": "indexer.hip"}
 def kernel_name(stage, wl, lay):
     """The kernel a stage's time is attributed to (the launcher's choice)."""
+    if stage == "indexer_topk":
+        return "indexer_topk_fused_kernel"
     if stage == "indexer":
         if not wl.fp8:
             return "indexer_f32_kernel"
@@ -330,9 +332,33 @@ def main():
         "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
         "mla": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
     }
+    # Where dsa_forward takes the fused indexer -> top-k kernel (prefill), time
+    # that call too: it replaces the first two stages inside `value`.
+    fused = wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and not wl.paged and lay.max_q_per_seq >= 8
+    if fused:
+        qi0, qs0, w0, _, ki0, ks0, _ = dw.sets[0]
+        nb = B.dsa_indexer_topk_workspace_size(dw.batch, dw.layout, dw.index_dtype, wl.h_i, wl.d_i, wl.top_k)
+        fws = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+        fbase = fws.data_ptr() + (-fws.data_ptr()) % 256
+
+        def fused_call():
+            B.dsa_indexer_topk(dw.batch, dw.layout, dw.index_dtype, wl.h_i, wl.d_i, qi0, qs0, w0, ki0, ks0,
+                               wl.index_scale, wl.top_k, dw.idx, fbase, nb, stream=stream)
+
+        fused_call()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for _ in range(steps):
+            fused_call()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        stage_ms["indexer_topk"] = f0.elapsed_time(f1) / steps
+        del fws
     work = stage_work(wl, lay)
+    work["indexer_topk"] = dict(work["indexer"])
     rooflines = {}
-    for st_name in ("indexer", "topk", "mla"):
+    for st_name in stage_ms:
         t_s = stage_ms[st_name] / 1e3
         wk = work[st_name]
         if decode or wk["peak_flops"] is None:

@@ -142,6 +142,32 @@ dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_
 dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t *bytes);
 
 /* ------------------------------------------------------------------------
+ * Stages 1 + 2 fused: the indices dsa_topk would write for the scores
+ * dsa_indexer_scores would write, without materialising the [T, n] score
+ * array where a fused kernel exists.  The top-k of a row is the top-k of the
+ * union of any partition of its keys, because every score depends on one key
+ * only ([G] Stage 1, item 3); the fused kernel streams each row's keys in
+ * ascending position and keeps a bounded list of candidates above a running
+ * threshold, selecting from it exactly (same ties, same order, -1 padding).
+ * It applies to FP8 keys with h_i == 64 and d_i == 128 in a contiguous
+ * cache, for batches with max_q_per_seq >= 8 (prefill, chunked prefill);
+ * its workspace holds (2k + 128, rounded up to 64) candidates of 8 bytes per
+ * query row.  Other shapes run the two stages with the fp32 score rows in
+ * the workspace.  Arguments as for the two stages; workspace 256-byte
+ * aligned, dsa_indexer_topk_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch, const dsa_kv_layout_t *keys,
+                              dsa_dtype_t dtype, int32_t h_i, int32_t d_i,
+                              const void *q_idx, const float *q_scale, const float *w,
+                              const void *k_idx, const float *k_scale, float scale,
+                              int32_t k, int32_t *indices,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+dsa_status_t dsa_indexer_topk_workspace_size(const dsa_batch_t *batch, const dsa_kv_layout_t *keys,
+                                             dsa_dtype_t dtype, int32_t h_i, int32_t d_i, int32_t k,
+                                             size_t *bytes);
+
+/* ------------------------------------------------------------------------
  * Stage 3: sparse MLA, absorbed (MQA) form ([G] Stage 2, gather and u_t
  * equations; logit of the classical MLA section).  For query row t and head
  * h, with J = { indices[t*k + j] : j < k, indices[t*k + j] >= 0 }:
@@ -176,7 +202,9 @@ dsa_status_t dsa_sparse_mla_workspace_size(const dsa_batch_t *batch, dsa_dtype_t
  * The whole path: indexer -> top-k -> sparse MLA, in the order of [G]'s
  * pipeline figure, enqueued back to back on one stream.  Both caches use the
  * same layout descriptor.  `scores` / `indices` may be NULL, in which case
- * they live in the workspace; otherwise the caller keeps them.
+ * they live in the workspace; otherwise the caller keeps them.  With
+ * `scores` NULL, shapes dsa_indexer_topk fuses take the fused kernel, and no
+ * score array exists at all.
  * ---------------------------------------------------------------------- */
 typedef struct {
   dsa_batch_t batch;

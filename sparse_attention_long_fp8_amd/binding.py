@@ -64,6 +64,10 @@ _SIGS = {
                                       ctypes.POINTER(c_size)],
     "dsa_forward": [ctypes.POINTER(dsa_forward_args_t), c_ptr, c_size, c_ptr],
     "dsa_forward_workspace_size": [ctypes.POINTER(dsa_forward_args_t), ctypes.POINTER(c_size)],
+    "dsa_indexer_topk": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32, c_i32,
+                         c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_f32, c_i32, c_ptr, c_ptr, c_size, c_ptr],
+    "dsa_indexer_topk_workspace_size": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32,
+                                        c_i32, c_i32, ctypes.POINTER(c_size)],
     "dsa_cache_append": [ctypes.POINTER(dsa_kv_layout_t), c_i32, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                          c_i32, c_ptr, c_ptr, c_ptr],
     "dsa_status_string": [c_i32],
@@ -207,6 +211,23 @@ def dsa_forward(args, workspace=None, workspace_bytes=0, stream=None, check=True
                            _stream(stream))
     if check:
         _check(st, "dsa_forward")
+    return st
+
+
+def dsa_indexer_topk_workspace_size(batch, keys, dtype, h_i, d_i, k):
+    n = c_size(0)
+    _check(lib().dsa_indexer_topk_workspace_size(ctypes.byref(batch), ctypes.byref(keys), dtype, h_i, d_i, int(k),
+                                                 ctypes.byref(n)), "dsa_indexer_topk_workspace_size")
+    return n.value
+
+
+def dsa_indexer_topk(batch, keys, dtype, h_i, d_i, q_idx, q_scale, w, k_idx, k_scale, scale, k, indices,
+                     workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().dsa_indexer_topk(ctypes.byref(batch), ctypes.byref(keys), dtype, h_i, d_i, _p(q_idx), _p(q_scale),
+                                _p(w), _p(k_idx), _p(k_scale), float(scale), int(k), _p(indices), _p(workspace),
+                                int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "dsa_indexer_topk")
     return st
 
 

@@ -22,6 +22,16 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
                               const float *k_scale, float scale, float *scores, int64_t ld,
                               hipStream_t stream);
 
+// Fused indexer -> top-k (FP8, 64 heads x 128, contiguous keys): candidate
+// list capacity per row and workspace bytes.
+int fused_topk_cap(int k);
+size_t fused_topk_workspace_bytes(int num_queries, int k);
+hipError_t launch_indexer_topk_fused(const BatchDev &bt, const int64_t *k_seq_start, int num_seqs,
+                                     int num_queries, int max_q_per_seq, const uint8_t *q,
+                                     const float *q_scale, const float *w, const uint8_t *k,
+                                     const float *k_scale, float scale, int topk, int32_t *indices,
+                                     void *workspace, hipStream_t stream);
+
 hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
                        int k, int32_t *indices, hipStream_t stream);
 

@@ -123,6 +123,46 @@ struct IdxTiledLds {
   int64_t page_row[kTPages];  // flat row of key 64p of the block
 };
 
+// Scores of one 32-key subtile of a staged stage for the QW rows of a wave:
+// lane key r (= 32*subtile + col), both half-waves end with the full sum.
+// The B fragments of key r: K-step ks holds its chunks 4ks + 2*half and
+// 4ks + 2*half + 1.  Every row is scored (a row past its candidate count
+// only on the causal diagonal; callers drop those), so that the MFMAs of one
+// row can overlap the ReLU/weight sum of another.
+template <int MT, int QW>
+__device__ __forceinline__ void score_subtile(const uint8_t *stage_keys, const float *stage_ksc, int r, int half,
+                                              const v8i (&a)[QW][MT][2], const float (&wr)[QW][MT][16],
+                                              const float (&row_scale)[QW], float (&out)[QW]) {
+  const uint8_t *kb = stage_keys + r * 128;
+  v8i bk[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = 4 * ks + 2 * half;
+    const v4i lo = *(const v4i *)(kb + 16 * (c ^ kswz(r)));
+    const v4i up = *(const v4i *)(kb + 16 * ((c + 1) ^ kswz(r)));
+    bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
+  }
+  const float ksc = stage_ksc[r];
+  v16f acc[QW][MT];
+#pragma unroll
+  for (int j = 0; j < QW; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][0], bk[0], v16f{}, 0, 0, 0, 127, 0, 127);
+      acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][1], bk[1], acc[j][mt], 0, 0, 0, 127, 0, 127);
+    }
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], relu(acc[j][mt][i]), sum);
+    sum = add_halves(sum);
+    out[j] = sum * row_scale[j] * ksc;
+  }
+}
+
 template <int MT, int QW>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
     BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
@@ -263,40 +303,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
 #pragma unroll
       for (int j = 0; j < QW; ++j) held[j][sub] = 0.f;
       if (!any) continue;  // uniform over the wave
-      // B fragments of keys sk0 .. sk0+31: lane key r = 32*sub + col,
-      // K-step ks holds chunks 4ks + 2*half and 4ks + 2*half + 1
-      const int r = 32 * sub + col;
-      const uint8_t *kb = sh.keys[buf] + r * 128;
-      v8i bk[2];
+      float sc[QW];
+      score_subtile<MT, QW>(sh.keys[buf], sh.ksc[buf], 32 * sub + col, half, a, wr, row_scale, sc);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c = 4 * ks + 2 * half;
-        const v4i lo = *(const v4i *)(kb + 16 * (c ^ kswz(r)));
-        const v4i up = *(const v4i *)(kb + 16 * ((c + 1) ^ kswz(r)));
-        bk[ks] = v8i{lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
-      }
-      const float ksc = sh.ksc[buf][r];
-      // every row is scored (a row past its candidate count only on the
-      // diagonal; those scores fall outside its store range), so that the
-      // MFMAs of one row can overlap the ReLU/weight sum of another
-      v16f acc[QW][MT];
-#pragma unroll
-      for (int j = 0; j < QW; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][0], bk[0], v16f{}, 0, 0, 0, 127, 0, 127);
-          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][mt][1], bk[1], acc[j][mt], 0, 0, 0, 127, 0, 127);
-        }
-#pragma unroll
-      for (int j = 0; j < QW; ++j) {
-        float sum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum = fmaf(wr[j][mt][i], relu(acc[j][mt][i]), sum);
-        sum = add_halves(sum);
-        held[j][sub] = sum * row_scale[j] * ksc;
-      }
+      for (int j = 0; j < QW; ++j) held[j][sub] = sc[j];
     }
     held_off = 4 * (si * kTStageKeys);
     // the next stage must have landed; later ones may stay in flight
@@ -304,6 +314,349 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
     lds_barrier();
   }
   store_held();
+}
+
+// --------------------------------------------------------------------------
+// Fused indexer -> top-k (prefill, contiguous keys).
+//
+// The top-k of a row is the top-k of the union of any partition of its keys,
+// because every score depends on one key only ("DeepSeek Sparse Attention DSA
+// Architecture Guide", "Stage 1: The Lightning Indexer", item 3).  A
+// workgroup takes QT = 4*QW rows of one sequence and streams ALL their keys,
+// in ascending position, through the staging of the tiled kernel above; the
+// scores are computed by the same code, so they are bit-identical to the
+// ones that kernel stores.  Instead of storing them, each row keeps a
+// candidate list in the workspace: (score, position) of every key whose
+// score beats the row's threshold tau, in ascending position.  Because keys
+// arrive in ascending position, a later key equal to tau can never displace
+// an earlier one (ties go to the lowest position), so the test is strict.
+// When a list could overflow its capacity, the wave that owns the row
+// selects the k best entries (score descending, position ascending) and
+// compacts them in place, in order; tau becomes the k-th score.  After the
+// last key the same selection writes the row's positions, ascending, to the
+// output, padded with -1 when the row has fewer than k keys.
+//
+// Selection (one wave, the row's list in global memory): an exact radix
+// select over order-preserving uint32 keys, four 8-bit digits from the top,
+// with a 256-bin LDS histogram per pass, gives tau and how many entries equal
+// to tau are kept (the first ones in list order); one ordered pass then keeps
+// the entries above tau and those first equal ones, with ballot prefix counts
+// for the write positions.
+// --------------------------------------------------------------------------
+struct IdxFusedLds {
+  uint8_t keys[kTBufs][kTStageBytes];
+  float ksc[kTBufs][kTStageKeys];
+  uint32_t hist[4][256];  // one radix histogram per wave
+};
+
+// Exclusive prefix over the wave's lanes, and wave total, of c in [0, 7].
+__device__ __forceinline__ void lane_prefix3(int c, int &before, int &total) {
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t m = __ballot((c >> bit) & 1);
+    before += lanes_below(m) << bit;
+    total += __popcll(m) << bit;
+  }
+}
+
+// Key (score order) and position of candidate i of a list, 4 per lane.
+__device__ __forceinline__ void load_cands(const float *cs, int n, int i, uint32_t (&key)[4], bool (&valid)[4]) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i + 3 < n) {
+    v = *(const float4 *)(cs + i);
+  } else {
+    if (i < n) v.x = cs[i];
+    if (i + 1 < n) v.y = cs[i + 1];
+    if (i + 2 < n) v.z = cs[i + 2];
+  }
+  const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    valid[e] = i + e < n;
+    key[e] = float_key(f[e]);
+  }
+}
+
+// The k-th largest key among the n (> k) candidates of a list, and how many
+// candidates equal to it belong to the k best.  Whole wave; uniform results.
+__device__ void wave_select_kth(const float *cs, int n, int k, uint32_t *hist, uint32_t &tau, int &need_eq) {
+  const int lane = lane_id();
+  uint32_t prefix = 0u, pmask = 0u;
+  int need = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[lane + 64 * q] = 0u;
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      uint32_t key[4];
+      bool valid[4];
+      load_cands(cs, n, i0 + 4 * lane, key, valid);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+    }
+    // lane l holds bins 255-4l .. 252-4l; scan them from the top
+    int c[4], sl = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = (int)hist[255 - 4 * lane - q];
+      sl += c[q];
+    }
+    int incl = sl;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __ballot(incl >= need);
+    const int L = hit ? __ffsll((unsigned long long)hit) - 1 : 63;  // empty only on NaN scores
+    int acc = incl - sl, digit = 255 - 4 * lane - 3;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= need) {
+        digit = 255 - 4 * lane - q;
+        found = true;
+      } else if (!found) {
+        acc += c[q];
+      }
+    }
+    digit = __shfl(digit, L, 64);
+    acc = __shfl(acc, L, 64);
+    need -= acc;
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 0xFFu << shift;
+  }
+  tau = prefix;
+  need_eq = need;
+}
+
+template <int MT, int QW>
+__global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
+    BatchDev bt, const int64_t *__restrict__ k_seq_start, const uint8_t *__restrict__ q,
+    const float *__restrict__ q_scale, const float *__restrict__ w, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, float scale, int topk, int cap, float *__restrict__ cand_s,
+    int32_t *__restrict__ cand_i, int32_t *__restrict__ indices) {
+  constexpr int H = 32 * MT;
+  constexpr int QT = 4 * QW;
+  constexpr int kSub = kTStageKeys / 32;
+  __shared__ IdxFusedLds sh;
+
+  const int b = blockIdx.y;
+  const int q0 = bt.q_seq_start[b];
+  const int nq = bt.q_seq_start[b + 1] - q0;
+  const int ngroups = (nq + QT - 1) / QT;
+  if ((int)blockIdx.x >= ngroups) return;
+  const int g0 = (ngroups - 1 - (int)blockIdx.x) * QT;  // longest rows first
+  const int kl = bt.k_len[b];
+  const int first_pos = kl - nq;
+  const int n_max = first_pos + min(nq, g0 + QT);
+  const int nst = (n_max + kTStageKeys - 1) / kTStageKeys;
+  const int64_t kbase = k_seq_start[b];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  int row_t[QW], row_n[QW];
+  v8i a[QW][MT][2];
+  float wr[QW][MT][16];
+  float row_scale[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    const int i = g0 + QW * wave + j;
+    const bool live = i < nq;
+    const int t = q0 + (live ? i : nq - 1);
+    row_t[j] = t;
+    row_n[j] = live ? first_pos + i + 1 : 0;
+    const uint8_t *qt = q + (int64_t)t * H * 128;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        a[j][mt][ks] = *(const v8i *)(qt + (32 * mt + col) * 128 + 64 * ks + 32 * half);
+    const float *wt = w + (int64_t)t * H;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = *(const float4 *)(wt + 32 * mt + 8 * r4 + 4 * half);
+        wr[j][mt][4 * r4 + 0] = v.x;
+        wr[j][mt][4 * r4 + 1] = v.y;
+        wr[j][mt][4 * r4 + 2] = v.z;
+        wr[j][mt][4 * r4 + 3] = v.w;
+      }
+    row_scale[j] = q_scale[t] * scale;
+  }
+  // (the barrier alone does not wait for global loads)
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  const uint32_t keys0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.keys[0][0]));
+  const uint32_t ksc0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.ksc[0][0]));
+  auto stage = [&](int si) __attribute__((always_inline)) {
+    const int buf = si % kTBufs;
+    const int s_stage = si * kTStageKeys;
+#pragma unroll
+    for (int m = 0; m < kTStageLoads / 4; ++m) {
+      const int j = wave + 4 * m;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t row = kbase + min(s_stage + r, n_max - 1);
+      lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kTStageBytes + 1024 * j);
+    }
+    if (wave < 2) {
+      const int64_t row = kbase + min(s_stage + 64 * wave + lane, n_max - 1);
+      lds_dma4_at(k_scale + row, ksc0 + buf * (kTStageKeys * 4) + 256 * wave);
+    }
+  };
+  constexpr int kLoads = kTStageLoads / 4;
+  auto wait_stages = [&](int o) __attribute__((always_inline)) {
+    if (wave < 2) {
+      if (o >= 2) wait_vmcnt<2 * (kLoads + 1)>(); else if (o == 1) wait_vmcnt<kLoads + 1>(); else wait_vmcnt<0>();
+    } else {
+      if (o >= 2) wait_vmcnt<2 * kLoads>(); else if (o == 1) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+    }
+  };
+
+  // candidate lists of this wave's rows
+  int cnt[QW];
+  uint32_t tau[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    cnt[j] = 0;
+    tau[j] = 0u;  // below every finite score's key
+  }
+
+  // keep the k best of row j's list (final: write their positions to the
+  // output instead, -1 padded)
+  auto select = [&](int j, bool final) __attribute__((always_inline)) {
+    float *cs = cand_s + (int64_t)row_t[j] * cap;
+    int32_t *ci = cand_i + (int64_t)row_t[j] * cap;
+    int32_t *out = indices + (int64_t)row_t[j] * topk;
+    const int n = cnt[j];
+    __threadfence_block();  // the list's stores by every lane of this wave are visible
+    const bool all = n <= topk;
+    uint32_t th = 0u;
+    int need_eq = 0;
+    if (!all) wave_select_kth(cs, n, topk, sh.hist[wave], th, need_eq);
+    int kept = 0, eq_seen = 0;
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      const int i = i0 + 4 * lane;
+      uint32_t key[4];
+      bool valid[4];
+      load_cands(cs, n, i, key, valid);
+      int idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) idx[e] = valid[e] ? ci[i + e] : -1;
+      float val[4];
+      if (!final) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = valid[e] ? cs[i + e] : 0.f;
+      }
+      bool gt[4], eq[4];
+      int ce = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gt[e] = valid[e] && (all || key[e] > th);
+        eq[e] = valid[e] && !all && key[e] == th;
+        ce += eq[e];
+      }
+      int pe, te;
+      lane_prefix3(ce, pe, te);
+      bool keep[4];
+      int run = eq_seen + pe, ck = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keep[e] = gt[e] || (eq[e] && run < need_eq);
+        run += eq[e];
+        ck += keep[e];
+      }
+      int pk, tk;
+      lane_prefix3(ck, pk, tk);
+      int pos = kept + pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keep[e]) {
+          if (final) {
+            out[pos] = idx[e];
+          } else {
+            cs[pos] = val[e];
+            ci[pos] = idx[e];
+          }
+          ++pos;
+        }
+      }
+      kept += tk;
+      eq_seen += te;
+    }
+    if (final) {
+      for (int p = kept + lane; p < topk; p += 64) out[p] = -1;
+    } else {
+      __threadfence_block();
+      cnt[j] = kept;
+      tau[j] = th;
+    }
+  };
+
+  // scores of the previous stage: appended to the lists at the start of the next one
+  float held[QW][kSub];
+  int held_s0 = 0;  // position of the held stage's key 0
+  auto emit_held = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < QW; ++j) {
+      if (held_s0 >= row_n[j]) continue;  // uniform
+      if (cnt[j] + kTStageKeys > cap) select(j, false);
+      float *cs = cand_s + (int64_t)row_t[j] * cap;
+      int32_t *ci = cand_i + (int64_t)row_t[j] * cap;
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+        const int s = held_s0 + 32 * sub + col;
+        const bool ok = half == 0 && s < row_n[j] && float_key(held[j][sub]) > tau[j];
+        const uint64_t m = __ballot(ok);
+        if (ok) {
+          const int p = cnt[j] + lanes_below(m);
+          cs[p] = held[j][sub];
+          ci[p] = s;
+        }
+        cnt[j] += __popcll(m);
+      }
+    }
+  };
+
+  for (int i = 0; i < kTBufs - 1 && i < nst; ++i) stage(i);
+  wait_stages(min(kTBufs - 2, nst - 1));
+  lds_barrier();
+
+  for (int si = 0; si < nst; ++si) {
+    const int buf = si % kTBufs;
+    if (si > 0) emit_held();
+    if (si + kTBufs - 1 < nst) stage(si + kTBufs - 1);
+    const int s_stage = si * kTStageKeys;
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int sk0 = s_stage + 32 * sub;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < QW; ++j) any |= sk0 < row_n[j];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) held[j][sub] = 0.f;
+      if (!any) continue;  // uniform over the wave
+      float sc[QW];
+      score_subtile<MT, QW>(sh.keys[buf], sh.ksc[buf], 32 * sub + col, half, a, wr, row_scale, sc);
+#pragma unroll
+      for (int j = 0; j < QW; ++j) held[j][sub] = sc[j];
+    }
+    held_s0 = s_stage;
+    wait_stages(min(si + kTBufs - 1, nst - 1) - (si + 1));
+    lds_barrier();
+  }
+  emit_held();
+#pragma unroll
+  for (int j = 0; j < QW; ++j)
+    if (row_n[j] > 0) select(j, true);
 }
 
 // --------------------------------------------------------------------------
@@ -466,6 +819,31 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
     wait_stages(min(si + kDecStageBufs, nst) - (si + 2));
     lds_barrier();
   }
+}
+
+int fused_topk_cap(int k) { return (2 * k + kTStageKeys + 63) / 64 * 64; }
+
+size_t fused_topk_workspace_bytes(int num_queries, int k) {
+  // candidate scores, then candidate positions (each 256-byte aligned)
+  const size_t one = ((size_t)num_queries * fused_topk_cap(k) * 4 + 255) / 256 * 256;
+  return 2 * one;
+}
+
+hipError_t launch_indexer_topk_fused(const BatchDev &bt, const int64_t *k_seq_start, int num_seqs,
+                                     int num_queries, int max_q_per_seq, const uint8_t *q,
+                                     const float *q_scale, const float *w, const uint8_t *k,
+                                     const float *k_scale, float scale, int topk, int32_t *indices,
+                                     void *workspace, hipStream_t stream) {
+  if (num_queries == 0) return hipSuccess;
+  constexpr int QW = 2;
+  const int cap = fused_topk_cap(topk);
+  const size_t one = ((size_t)num_queries * cap * 4 + 255) / 256 * 256;
+  float *cand_s = (float *)workspace;
+  int32_t *cand_i = (int32_t *)((char *)workspace + one);
+  const dim3 grid((max_q_per_seq + 4 * QW - 1) / (4 * QW), num_seqs);
+  hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, k_seq_start, q,
+                     q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
+  return hipGetLastError();
 }
 
 hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,

@@ -148,9 +148,26 @@ size_t mla_ws(const dsa_batch_t *bt, dsa_dtype_t dt, int32_t heads, int32_t d_v,
   return dsa::mla_bf16_workspace_bytes(bt->num_queries, heads, d_v, k);
 }
 
-// Workspace carve-up of dsa_forward: [scores][indices][mla partials], 256-byte aligned.
+// The fused indexer -> top-k kernel covers FP8 keys of 64 heads x 128 in a
+// contiguous cache, for batches with at least 8 query rows per sequence.
+bool fused_applies(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i, int32_t d_i) {
+  return dt == DSA_FP8_E4M3 && h_i == 64 && d_i == 128 && !ly->paged && bt->max_q_per_seq >= 8;
+}
+
+// Workspace of dsa_indexer_topk: the fused kernel's candidate lists, or the
+// fp32 score rows the two separate stages pass between them.
+size_t indexer_topk_ws(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i, int32_t d_i,
+                       int32_t k) {
+  if (fused_applies(bt, ly, dt, h_i, d_i)) return dsa::fused_topk_workspace_bytes(bt->num_queries, k);
+  return round_up((size_t)bt->num_queries * round_up((size_t)bt->max_k_len, 4) * sizeof(float), 256);
+}
+
+// Workspace carve-up of dsa_forward: [scores or fused candidate lists][indices][mla partials],
+// 256-byte aligned.  Without caller-kept scores, shapes the fused indexer -> top-k kernel
+// covers use it, and the region holds its candidate lists instead of the score rows.
 struct ForwardWs {
   int64_t ld;
+  bool fused;
   size_t scores_off, indices_off, mla_off, total;
 };
 
@@ -158,9 +175,13 @@ ForwardWs forward_ws(const dsa_forward_args_t *a) {
   ForwardWs w{};
   const size_t T = (size_t)a->batch.num_queries;
   w.ld = a->scores ? a->ld_scores : (int64_t)round_up((size_t)a->batch.max_k_len, 4);
+  w.fused = !a->scores && fused_applies(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i);
   size_t off = 0;
   w.scores_off = off;
-  if (!a->scores) off += round_up(T * (size_t)w.ld * sizeof(float), 256);
+  if (w.fused)
+    off += round_up(dsa::fused_topk_workspace_bytes(a->batch.num_queries, a->top_k), 256);
+  else if (!a->scores)
+    off += round_up(T * (size_t)w.ld * sizeof(float), 256);
   w.indices_off = off;
   if (!a->indices) off += round_up(T * (size_t)a->top_k * sizeof(int32_t), 256);
   w.mla_off = off;
@@ -297,13 +318,59 @@ dsa_status_t dsa_forward(const dsa_forward_args_t *a, void *workspace, size_t wo
   void *mla_ws_ptr = base ? base + ws.mla_off : nullptr;
   const size_t mla_bytes = ws.total - ws.mla_off;
 
-  st = dsa_indexer_scores(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w, a->k_idx,
-                          a->k_scale, a->index_scale, scores, ws.ld, stream);
-  if (st != DSA_OK) return st;
-  st = dsa_topk(&a->batch, scores, ws.ld, a->top_k, indices, nullptr, 0, stream);
-  if (st != DSA_OK) return st;
+  if (ws.fused) {
+    st = dsa_indexer_topk(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w,
+                          a->k_idx, a->k_scale, a->index_scale, a->top_k, indices, base + ws.scores_off,
+                          ws.indices_off - ws.scores_off, stream);
+    if (st != DSA_OK) return st;
+  } else {
+    st = dsa_indexer_scores(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w,
+                            a->k_idx, a->k_scale, a->index_scale, scores, ws.ld, stream);
+    if (st != DSA_OK) return st;
+    st = dsa_topk(&a->batch, scores, ws.ld, a->top_k, indices, nullptr, 0, stream);
+    if (st != DSA_OK) return st;
+  }
   return dsa_sparse_mla_fwd(&a->batch, &a->layout, a->mla_dtype, a->heads, a->d_qk, a->d_v, a->q, a->kv, indices,
                             a->top_k, a->sm_scale, a->out, a->lse, mla_ws_ptr, mla_bytes, stream);
+}
+
+dsa_status_t dsa_indexer_topk_workspace_size(const dsa_batch_t *batch, const dsa_kv_layout_t *keys, dsa_dtype_t dtype,
+                                             int32_t h_i, int32_t d_i, int32_t k, size_t *bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  dsa_status_t st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (!keys) return fail(DSA_ERR_INVALID_ARGUMENT, "key layout is NULL");
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "k must be in [1, 65536] (got %d)", k);
+  *bytes = indexer_topk_ws(batch, keys, dtype, h_i, d_i, k);
+  return ok();
+}
+
+dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch, const dsa_kv_layout_t *keys, dsa_dtype_t dtype, int32_t h_i,
+                              int32_t d_i, const void *q_idx, const float *q_scale, const float *w, const void *k_idx,
+                              const float *k_scale, float scale, int32_t k, int32_t *indices, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t st = check_indexer(batch, keys, dtype, h_i, d_i, q_idx, q_scale, w, k_idx, k_scale, scale,
+                                  (const float *)1, batch ? batch->max_k_len : 0);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "k must be in [1, 65536] (got %d)", k);
+  if (batch->num_queries > 0 && !indices) return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+  const size_t need = indexer_topk_ws(batch, keys, dtype, h_i, d_i, k);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "indexer + top-k needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  if (need && !aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (batch->num_queries == 0) return ok();
+  if (fused_applies(batch, keys, dtype, h_i, d_i))
+    return hip_status(dsa::launch_indexer_topk_fused(to_dev(batch), keys->k_seq_start, batch->num_seqs,
+                                                      batch->num_queries, batch->max_q_per_seq,
+                                                      (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx,
+                                                      k_scale, scale, k, indices, workspace, stream),
+                      "fused indexer + top-k launch");
+  const int64_t ld = (int64_t)round_up((size_t)batch->max_k_len, 4);
+  st = dsa_indexer_scores(batch, keys, dtype, h_i, d_i, q_idx, q_scale, w, k_idx, k_scale, scale, (float *)workspace,
+                          ld, stream);
+  if (st != DSA_OK) return st;
+  return dsa_topk(batch, (const float *)workspace, ld, k, indices, nullptr, 0, stream);
 }
 
 dsa_status_t dsa_cache_append(const dsa_kv_layout_t *ly, int32_t num_tokens, const int32_t *seq, const int32_t *pos,

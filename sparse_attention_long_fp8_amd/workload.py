@@ -123,13 +123,15 @@ class DeviceWorkload:
 
     def prepare_forward(self):
         """Argument blocks of the fused entry point for every input copy, and
-        its workspace, built once so that a timed loop only makes the call."""
+        its workspace, built once so that a timed loop only makes the call.
+        The scores are not kept, so shapes with a fused indexer -> top-k
+        kernel take it (the indices are kept)."""
         wl = self.wl
         self._fwd_args = []
         for qi, qs, w, q, ki, ks, kv in self.sets:
             self._fwd_args.append(B.forward_args(
                 self.batch, self.layout, index_dtype=self.index_dtype, h_i=wl.h_i, d_i=wl.d_i, q_idx=qi, q_scale=qs,
-                w=w, k_idx=ki, k_scale=ks, index_scale=wl.index_scale, top_k=wl.top_k, scores=self.scores,
+                w=w, k_idx=ki, k_scale=ks, index_scale=wl.index_scale, top_k=wl.top_k, scores=None,
                 ld_scores=self.ld, indices=self.idx, mla_dtype=self.mla_dtype, heads=wl.heads, d_qk=wl.d_qk,
                 d_v=wl.d_v, q=q, kv=kv, sm_scale=wl.sm_scale, out=self.out, lse=self.lse))
         need = max(B.dsa_forward_workspace_size(a) for a in self._fwd_args)
@@ -140,13 +142,15 @@ class DeviceWorkload:
         """One pass through dsa_forward with the prepared arguments."""
         B.dsa_forward(self._fwd_args[copy % self.copies], self._fwd_ws, self._fwd_need, stream=stream)
 
-    def forward(self, copy=0, stream=None):
-        """The same pass through the fused dsa_forward entry point."""
+    def forward(self, copy=0, stream=None, keep_scores=True):
+        """The same pass through the fused dsa_forward entry point (without
+        kept scores, shapes with a fused indexer -> top-k kernel take it)."""
         wl = self.wl
         qi, qs, w, q, ki, ks, kv = self.sets[copy % self.copies]
         args = B.forward_args(self.batch, self.layout, index_dtype=self.index_dtype, h_i=wl.h_i, d_i=wl.d_i,
                               q_idx=qi, q_scale=qs, w=w, k_idx=ki, k_scale=ks, index_scale=wl.index_scale,
-                              top_k=wl.top_k, scores=self.scores, ld_scores=self.ld, indices=self.idx,
+                              top_k=wl.top_k, scores=self.scores if keep_scores else None, ld_scores=self.ld,
+                              indices=self.idx,
                               mla_dtype=self.mla_dtype, heads=wl.heads, d_qk=wl.d_qk, d_v=wl.d_v, q=q, kv=kv,
                               sm_scale=wl.sm_scale, out=self.out, lse=self.lse)
         need = B.dsa_forward_workspace_size(args)

@@ -152,3 +152,16 @@ def test_fused_forward_equals_stages(full):
     torch.cuda.synchronize()
     assert torch.equal(dw.idx, idx0)
     assert torch.equal(dw.out.view(torch.int16), out0.view(torch.int16)) and torch.equal(dw.lse, lse0)
+
+
+def test_forward_without_kept_scores_equals_stages(full):
+    """dsa_forward with no score array (prefill: the fused indexer -> top-k
+    kernel) selects exactly the stages' indices and so gives the same output."""
+    dw = full
+    dw.step()
+    idx0, out0, lse0 = dw.idx.clone(), dw.out.clone(), dw.lse.clone()
+    dw.idx.fill_(-7)
+    dw.forward(keep_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.idx, idx0)
+    assert torch.equal(dw.out.view(torch.int16), out0.view(torch.int16)) and torch.equal(dw.lse, lse0)
