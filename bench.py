@@ -47,9 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel on MIB mebibytes (counter calibration) and exit")
-    ap.add_argument("--op", default="forward", choices=["forward", "cache_append"],
+    ap.add_argument("--op", default="forward", choices=["forward", "cache_append", "output_projection"],
                     help="forward: the hot path (default); cache_append: the decode-step cache append "
-                         "(--workload append_prefill_16k | append_decode_64)")
+                         "(--workload append_prefill_16k | append_decode_64); output_projection: W_UV then W_O "
+                         "(--workload proj_decode_32 | proj_prefill_16k)")
     return ap.parse_args()
 
 
@@ -269,6 +270,71 @@ def bench_cache_append(args):
     print(json.dumps(result))
 
 
+PROJ_WORKLOADS = {"proj_decode_32": 32, "proj_prefill_16k": 16384}
+
+
+def bench_output_projection(args):
+    """Times dsa_output_projection (DeepSeek-V3 widths: 128 heads, d_c 512,
+    d_h 128, hidden 7168) and prints one JSON line (its own metric)."""
+    import torch
+    from sparse_attention_long_fp8_amd import binding as B
+
+    name = args.workload if args.workload in PROJ_WORKLOADS else "proj_prefill_16k"
+    T = PROJ_WORKLOADS[name]
+    H, d_c, d_h, hidden = 128, 512, 128, 7168
+    decode = T <= 64
+    steps = args.steps if args.steps is not None else (200 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    dev = torch.device("cuda:0")
+    B.lib()
+    g = torch.Generator(device=dev).manual_seed(5)
+    o = torch.randn(T, H, d_c, device=dev, generator=g).to(torch.bfloat16)
+    w_uv = (torch.randn(H * d_h, d_c, device=dev, generator=g) / d_c ** 0.5).to(torch.bfloat16)
+    # weights rotate over copies so that decode steps stream them from HBM
+    copies = 2 if decode else 1
+    w_o = [(torch.randn(hidden, H * d_h, device=dev, generator=g) / (H * d_h) ** 0.5).to(torch.bfloat16)
+           for _ in range(copies)]
+    out = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    nb = B.dsa_output_projection_workspace_size(T, H, d_h)
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    h = B.dsa_blaslt_create()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        B.dsa_output_projection(h, T, H, d_c, d_h, hidden, o, w_uv, w_o[i % copies], out, base, nb, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    B.dsa_blaslt_destroy(h)
+    flops = 2.0 * T * (H * d_h * d_c + hidden * H * d_h)
+    nbytes = 2.0 * (H * d_h * d_c + hidden * H * d_h + T * H * d_c + T * hidden + 2 * T * H * d_h)
+    if decode:
+        roof = {"bound": "hbm", "achieved": nbytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": nbytes / (ms / 1e3) / HBM_PEAK}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / (ms / 1e3) / 1e12, "peak": BF16_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / BF16_PEAK}
+    roof.update({"traffic": None, "kernel": "hipBLASLt GEMMs (W_UV batched over heads, then W_O)",
+                 "flops": flops, "bytes": nbytes})
+    print(json.dumps({
+        "metric": "query-tokens/sec through the output projections (W_UV per head, then W_O)",
+        "value": T / (ms / 1e3), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "queries": T, "heads": H, "d_c": d_c, "d_h": d_h, "hidden": hidden,
+                   "weight_copies": copies},
+        "roofline": roof, "cpu_baseline": None}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -281,6 +347,9 @@ def main():
         return
     if args.op == "cache_append":
         bench_cache_append(args)
+        return
+    if args.op == "output_projection":
+        bench_output_projection(args)
         return
     from sparse_attention_long_fp8_amd import binding as B
     from sparse_attention_long_fp8_amd import synth

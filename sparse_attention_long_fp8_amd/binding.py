@@ -70,6 +70,11 @@ _SIGS = {
                                         c_i32, c_i32, ctypes.POINTER(c_size)],
     "dsa_cache_append": [ctypes.POINTER(dsa_kv_layout_t), c_i32, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                          c_i32, c_ptr, c_ptr, c_ptr],
+    "dsa_output_projection": [c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size,
+                              c_ptr],
+    "dsa_output_projection_workspace_size": [c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
+    "dsa_blaslt_create": [ctypes.POINTER(c_ptr)],
+    "dsa_blaslt_destroy": [c_ptr],
     "dsa_status_string": [c_i32],
     "dsa_last_error": [],
     "dsa_abi_version": [],
@@ -238,6 +243,33 @@ def dsa_cache_append(layout, num_tokens, seq, pos, d_i, k_new, k_pool, k_scale_p
                                 _stream(stream))
     if check:
         _check(st, "dsa_cache_append")
+    return st
+
+
+def dsa_blaslt_create():
+    h = c_ptr()
+    _check(lib().dsa_blaslt_create(ctypes.byref(h)), "dsa_blaslt_create")
+    return h.value
+
+
+def dsa_blaslt_destroy(handle):
+    _check(lib().dsa_blaslt_destroy(handle), "dsa_blaslt_destroy")
+
+
+def dsa_output_projection_workspace_size(num_queries, heads, d_h):
+    n = c_size(0)
+    _check(lib().dsa_output_projection_workspace_size(int(num_queries), int(heads), int(d_h), ctypes.byref(n)),
+           "dsa_output_projection_workspace_size")
+    return n.value
+
+
+def dsa_output_projection(blaslt, num_queries, heads, d_c, d_h, hidden, o, w_uv, w_o, out, workspace,
+                          workspace_bytes, stream=None, check=True):
+    st = lib().dsa_output_projection(blaslt, int(num_queries), int(heads), int(d_c), int(d_h), int(hidden), _p(o),
+                                     _p(w_uv), _p(w_o), _p(out), _p(workspace), int(workspace_bytes),
+                                     _stream(stream))
+    if check:
+        _check(st, "dsa_output_projection")
     return st
 
 

@@ -24,7 +24,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
-LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "libdsa.cpp"]
+LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "libdsa.cpp", "projection.cpp"]
+# the output projections are plain GEMMs, run by hipBLASLt
+LIB_LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 # Per-source flags.  The FP8 indexer reads every MFMA result with VALU code
 # (ReLU, head weights); keeping the accumulators in ordinary VGPRs saves one
@@ -83,9 +85,9 @@ def _compile(src, verbose):
     return obj
 
 
-def _link(objs, out, verbose):
+def _link(objs, out, verbose, libs=()):
     tmp = out + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + list(libs), verbose)
     os.replace(tmp, out)
 
 
@@ -94,7 +96,7 @@ def build(verbose: bool = False) -> str:
     srcs = LIB_SOURCES + PROBE_SOURCES
     with ThreadPoolExecutor(min(len(srcs), 8)) as ex:
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
-    _link([objs[s] for s in LIB_SOURCES], LIB_PATH, verbose)
+    _link([objs[s] for s in LIB_SOURCES], LIB_PATH, verbose, LIB_LINK)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_PATH, verbose)
     return LIB_PATH
 

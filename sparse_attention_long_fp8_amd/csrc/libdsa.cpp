@@ -192,6 +192,21 @@ ForwardWs forward_ws(const dsa_forward_args_t *a) {
 
 }  // namespace
 
+namespace dsa {
+// Status reporting for the other host sources of the library (records the
+// message dsa_last_error() returns; DSA_OK clears it).
+dsa_status_t report(dsa_status_t st, const char *fmt, ...) {
+  if (st == DSA_OK) return ok();
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+}  // namespace dsa
+
 extern "C" {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
