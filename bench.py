@@ -47,10 +47,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel on MIB mebibytes (counter calibration) and exit")
-    ap.add_argument("--op", default="forward", choices=["forward", "cache_append", "output_projection"],
+    ap.add_argument("--op", default="forward",
+                    choices=["forward", "cache_append", "output_projection", "module_forward"],
                     help="forward: the hot path (default); cache_append: the decode-step cache append "
                          "(--workload append_prefill_16k | append_decode_64); output_projection: W_UV then W_O "
-                         "(--workload proj_decode_32 | proj_prefill_16k)")
+                         "(--workload proj_decode_32 | proj_prefill_16k); module_forward: the complete fp32 "
+                         "module at its verification shape (--workload module_2x16k)")
     return ap.parse_args()
 
 
@@ -335,6 +337,104 @@ def bench_output_projection(args):
         "roofline": roof, "cpu_baseline": None}))
 
 
+MODULE_WORKLOADS = {"module_2x16k": dict(B=2, S=16384, hidden=1024, H=16, d_h=64, d_c=256, d_i=32, top_k=512)}
+
+
+def module_cpu_baseline(c, budget_s):
+    """The oracle's module (float64 numpy) on whole batch elements of the
+    same shape until budget_s seconds of oracle time have passed."""
+    from oracle import module_oracle as M
+    rng = np.random.default_rng(11)
+    lin = lambda o, i: rng.uniform(-i ** -0.5, i ** -0.5, (o, i)).astype(np.float32)
+    hidden, H, d_h, d_c, d_i = c["hidden"], c["H"], c["d_h"], c["d_c"], c["d_i"]
+    W = [lin(d_i, hidden), lin(d_i, hidden), lin(H * d_h, hidden), lin(H * d_h, d_c), lin(H * d_h, d_c),
+         lin(hidden, H * d_h)]
+    qh = rng.standard_normal((1, hidden)).astype(np.float32)
+    hist = rng.standard_normal((1, c["S"], hidden)).astype(np.float32)
+    lat = rng.standard_normal((1, c["S"], d_c)).astype(np.float32)
+    done, elapsed = 0, 0.0
+    while elapsed < budget_s:  # one input set, reused: generating it is not timed and costs more than a call
+        t0 = time.perf_counter()
+        M.module_forward(qh, hist, lat, *W, c["top_k"], H, d_h)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(i["num_threads"] for i in blas) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"value": done / elapsed, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d calls on one batch element (one query over a %d-token history), the whole module; "
+                      "float64 numpy; %.1f s of oracle time" % (done, c["S"], elapsed)}
+
+
+def bench_module_forward(args):
+    """Times dsa_module_forward (fp32: indexer projections, indexer scores,
+    top-k, query projection and W_UK absorption, sparse softmax over latent
+    rows, W_UV and W_out) at the verification shape of the module's page and
+    prints one JSON line (its own metric)."""
+    import torch
+    from sparse_attention_long_fp8_amd import binding as B
+
+    name = args.workload if args.workload in MODULE_WORKLOADS else "module_2x16k"
+    c = MODULE_WORKLOADS[name]
+    Bn, S, hidden, H, d_h, d_c, d_i, k = (c[x] for x in ("B", "S", "hidden", "H", "d_h", "d_c", "d_i", "top_k"))
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 10
+    dev = torch.device("cuda:0")
+    B.lib()
+    g = torch.Generator(device=dev).manual_seed(9)
+    lin = lambda o, i: (torch.rand(o, i, device=dev, generator=g) * 2 - 1) * i ** -0.5
+    W = [lin(d_i, hidden), lin(d_i, hidden), lin(H * d_h, hidden), lin(H * d_h, d_c), lin(H * d_h, d_c),
+         lin(hidden, H * d_h)]
+    # three copies of the history (3 x 134 MB) rotate so that every step reads it from HBM, not the
+    # 256 MB last-level cache
+    copies = 3
+    qh = [torch.randn(Bn, hidden, device=dev, generator=g) for _ in range(copies)]
+    hist = [torch.randn(Bn, S, hidden, device=dev, generator=g) for _ in range(copies)]
+    lat = [torch.randn(Bn, S, d_c, device=dev, generator=g) for _ in range(copies)]
+    out = torch.empty(Bn, hidden, device=dev)
+    idx = torch.empty(Bn, k, dtype=torch.int32, device=dev)
+    nb = B.dsa_module_forward_workspace_size(Bn, S, H, d_h, d_c, d_i)
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device=dev)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    h = B.dsa_blaslt_create()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % copies
+        B.dsa_module_forward(h, Bn, S, hidden, H, d_h, d_c, d_i, k, qh[j], hist[j], lat[j], *W, out, idx, base, nb,
+                             stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    B.dsa_blaslt_destroy(h)
+    m = min(k, S)
+    weights = d_i * hidden * 2 + H * d_h * hidden + 2 * H * d_h * d_c + hidden * H * d_h
+    nbytes = 4.0 * (Bn * S * hidden + Bn * S * d_i * 2 + Bn * m * d_c + weights + 2 * Bn * hidden)
+    cpu = None if args.no_cpu_baseline else module_cpu_baseline(c, args.cpu_budget)
+    print(json.dumps({
+        "metric": "query-tokens/sec through the complete DSA module (fp32)",
+        "value": Bn / (ms / 1e3), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, **c, "input_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": nbytes / (ms / 1e3) / HBM_PEAK, "traffic": None,
+                     "kernel": "whole step (its bytes are the history read by the indexer-key GEMM)",
+                     "bytes": nbytes},
+        "cpu_baseline": cpu}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,6 +450,9 @@ def main():
         return
     if args.op == "output_projection":
         bench_output_projection(args)
+        return
+    if args.op == "module_forward":
+        bench_module_forward(args)
         return
     from sparse_attention_long_fp8_amd import binding as B
     from sparse_attention_long_fp8_amd import synth

@@ -181,12 +181,14 @@ dsa_status_t dsa_indexer_topk_workspace_size(const dsa_batch_t *batch, const dsa
  * out = 0 and lse = -inf.  Indices are positions within the query's
  * sequence (as written by dsa_topk) and must be < n_t.
  *   dtype  DSA_BF16 (q, kv, out bf16; heads 16, 32, 64 or 128, d_qk == 576,
- *          d_v == 512) or DSA_F32 (heads <= 64, d_qk <= 128, d_v <= d_qk).
+ *          d_v == 512) or DSA_F32 (heads <= 64, d_qk <= 256, d_v <= d_qk).
  *   q      [T, heads, d_qk];  kv contiguous [num_rows, d_qk] or paged
  *          [pages, page_size, d_qk];  indices [T, k] int32
  *   out    [T, heads, d_v] (dtype);  lse [T, heads] fp32, may be NULL
- *   workspace: dsa_sparse_mla_workspace_size() bytes (split partials for
- *          small batches; may be 0).
+ *   workspace: dsa_sparse_mla_workspace_size() bytes, 16-byte aligned:
+ *          the partials of rows whose selection is split over several
+ *          workgroups when there are too few rows to fill the GPU (either
+ *          dtype); 0 when no row is split.
  * ---------------------------------------------------------------------- */
 dsa_status_t dsa_sparse_mla_fwd(const dsa_batch_t *batch, const dsa_kv_layout_t *kv_layout,
                                 dsa_dtype_t dtype, int32_t heads, int32_t d_qk, int32_t d_v,
@@ -301,8 +303,45 @@ dsa_status_t dsa_output_projection(void *blaslt, int32_t num_queries, int32_t he
 dsa_status_t dsa_output_projection_workspace_size(int32_t num_queries, int32_t heads, int32_t d_h,
                                                   size_t *bytes);
 
-/* A hipBLASLt handle for dsa_output_projection (host and device resources
- * of the GEMM library; the caller owns it and destroys it). */
+/* ------------------------------------------------------------------------
+ * The page's complete DSA module ([G] "End-to-End Implementation": the
+ * DeepSeekSparseAttention module with its LightningIndexer), fp32, one query
+ * token per batch element over a history of seq_len tokens:
+ *
+ *   k_I[b, s] = hist[b, s] . w_ki^T;   q_I[b] = q_hidden[b] . w_qi^T
+ *   I[b, s]   = ReLU(q_I[b] . k_I[b, s]) / sqrt(index_dim)
+ *   indices[b] = the min(top_k, seq_len) best s, ascending (ties: lowest s), -1 padded
+ *   per head h: o_h = softmax_s(q_h . K_h[s] / sqrt(head_dim)) . V_h[s] over the
+ *               selection, with q = q_hidden . w_q^T, K = c . w_uk^T, V = c . w_uv^T,
+ *               c = latent[b, s]
+ *   out[b]   = concat_h o_h . w_out^T
+ *
+ * The page decompresses K and V per selected token; this computes the same
+ * function with W_UK folded into the query and W_UV applied after the
+ * softmax (hipBLASLt GEMMs, the fp32 indexer, top-k and sparse-MLA kernels).
+ *   q_hidden [batch, hidden]; hist [batch, seq_len, hidden];
+ *   latent [batch, seq_len, latent_dim] (<= 256); w_qi, w_ki [index_dim, hidden]
+ *   (index_dim <= 128); w_q, w_uk, w_uv [heads * head_dim, hidden | latent_dim]
+ *   (heads <= 64); w_out [hidden, heads * head_dim]; out [batch, hidden];
+ *   indices [batch, top_k] int32.  All fp32 except indices.
+ *   workspace: 256-byte aligned, dsa_module_forward_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+dsa_status_t dsa_module_forward(void *blaslt, int32_t batch, int32_t seq_len, int32_t hidden,
+                                int32_t heads, int32_t head_dim, int32_t latent_dim,
+                                int32_t index_dim, int32_t top_k, const float *q_hidden,
+                                const float *hist, const float *latent, const float *w_qi,
+                                const float *w_ki, const float *w_q, const float *w_uk,
+                                const float *w_uv, const float *w_out, float *out,
+                                int32_t *indices, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+dsa_status_t dsa_module_forward_workspace_size(int32_t batch, int32_t seq_len, int32_t heads,
+                                               int32_t head_dim, int32_t latent_dim,
+                                               int32_t index_dim, size_t *bytes);
+
+/* A hipBLASLt handle for dsa_output_projection and dsa_module_forward (host
+ * and device resources of the GEMM library; the caller owns it and destroys
+ * it). */
 dsa_status_t dsa_blaslt_create(void **handle);
 dsa_status_t dsa_blaslt_destroy(void *handle);
 

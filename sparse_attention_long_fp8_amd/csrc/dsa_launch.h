@@ -40,10 +40,16 @@ hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores,
 int mla_bf16_splits(int num_queries, int heads, int k);
 size_t mla_bf16_workspace_bytes(int num_queries, int heads, int d_v, int k);
 
+// Split count and workspace of the fp32 sparse-MLA kernel (1 split = no
+// workspace).
+int mla_f32_splits(int num_queries, int k);
+size_t mla_f32_workspace_bytes(int num_queries, int heads, int d_v, int k);
+size_t mla_f32_workspace_bound(int num_queries, int heads, int d_v);  // over every k
+
 hipError_t launch_mla_f32(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
                           int d_qk, int d_v, const float *q, const float *kv,
                           const int32_t *indices, int k, float sm_scale, float *out, float *lse,
-                          hipStream_t stream);
+                          void *workspace, hipStream_t stream);
 
 hipError_t launch_mla_bf16(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
                            const void *q, const void *kv, const int32_t *indices, int k,

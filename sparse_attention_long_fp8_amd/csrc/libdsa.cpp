@@ -133,8 +133,8 @@ dsa_status_t check_mla(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dty
       return fail(DSA_ERR_UNSUPPORTED, "bf16 sparse MLA: heads must be 16, 32, 64 or 128 (got %d)", heads);
     if (!aligned(q, 16) || !aligned(kv, 16)) return fail(DSA_ERR_INVALID_ARGUMENT, "bf16 q / kv must be 16-byte aligned");
   } else if (dt == DSA_F32) {
-    if (heads < 1 || d_qk < 1 || d_qk > 128 || d_v < 1 || d_v > d_qk)
-      return fail(DSA_ERR_UNSUPPORTED, "f32 sparse MLA: needs heads >= 1, 1 <= d_v <= d_qk <= 128");
+    if (heads < 1 || heads > 64 || d_qk < 1 || d_qk > 256 || d_v < 1 || d_v > d_qk)
+      return fail(DSA_ERR_UNSUPPORTED, "f32 sparse MLA: needs 1 <= heads <= 64, 1 <= d_v <= d_qk <= 256");
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "sparse MLA dtype must be DSA_F32 or DSA_BF16");
   }
@@ -144,6 +144,7 @@ dsa_status_t check_mla(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dty
 }
 
 size_t mla_ws(const dsa_batch_t *bt, dsa_dtype_t dt, int32_t heads, int32_t d_v, int32_t k) {
+  if (dt == DSA_F32) return dsa::mla_f32_workspace_bytes(bt->num_queries, heads, d_v, k);
   if (dt != DSA_BF16) return 0;
   return dsa::mla_bf16_workspace_bytes(bt->num_queries, heads, d_v, k);
 }
@@ -296,7 +297,7 @@ dsa_status_t dsa_sparse_mla_fwd(const dsa_batch_t *batch, const dsa_kv_layout_t 
                              stream);
   else
     e = dsa::launch_mla_f32(bt, kd, batch->num_queries, heads, d_qk, d_v, (const float *)q, (const float *)kv,
-                            indices, k, sm_scale, (float *)out, lse, stream);
+                            indices, k, sm_scale, (float *)out, lse, workspace, stream);
   return hip_status(e, "sparse MLA launch");
 }
 

@@ -1,5 +1,5 @@
 // Test-only probes of gfx950 instruction semantics the libdsa kernels rely
-// on: FP8 and bf16 MFMA operand / accumulator lane layouts (and with them the
+// on: FP8, bf16 and fp32 MFMA operand / accumulator lane layouts (and with them the
 // FP8 E4M3 interpretation of bytes) and the lane mapping of the LDS transpose
 // read.  One wave each, fully in bounds; built into libdsa_probe.so, which
 // only the test-suite loads.
@@ -34,6 +34,14 @@ __global__ void probe_bf16_32x32x16_kernel(const v8bf *a, const v8bf *b, v16f *d
   const int l = threadIdx.x;
   v16f acc = {};
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[l], b[l], acc, 0, 0, 0);
+  d[l] = acc;
+}
+
+// a, b: [64] fp32; d: [64][4]
+__global__ void probe_f32_16x16x4_kernel(const float *a, const float *b, v4f *d) {
+  const int l = threadIdx.x;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[l], b[l], acc, 0, 0, 0);
   d[l] = acc;
 }
 
@@ -80,6 +88,12 @@ int dsa_probe_bf16_16x16x32(const void *a, const void *b, float *d, hipStream_t 
 int dsa_probe_bf16_32x32x16(const void *a, const void *b, float *d, hipStream_t stream) {
   hipLaunchKernelGGL(probe_bf16_32x32x16_kernel, dim3(1), dim3(64), 0, stream, (const v8bf *)a,
                      (const v8bf *)b, (v16f *)d);
+  return (int)hipGetLastError();
+}
+
+int dsa_probe_f32_16x16x4(const void *a, const void *b, float *d, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_f32_16x16x4_kernel, dim3(1), dim3(64), 0, stream, (const float *)a,
+                     (const float *)b, (v4f *)d);
   return (int)hipGetLastError();
 }
 

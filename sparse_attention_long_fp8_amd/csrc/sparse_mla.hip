@@ -20,70 +20,258 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // --------------------------------------------------------------------------
-// fp32 path (heads <= 64, d_qk <= 128, d_v <= d_qk): one wave per (t, h).
-// Lanes take 64 selected tokens at a time for the logits; each lane then
-// owns output dims lane and lane + 64.
+// fp32 path (1 <= heads <= 64, d_v <= d_qk <= 256).
+//
+// A workgroup of 4 waves takes every head of one query row over a range of
+// its selected slots, 64 slots (one chunk) at a time, so that each gathered
+// row is read from memory once for all heads:
+//   * the 64 rows of the chunk go to LDS (zero-filled past d_qk and for
+//     slots that select nothing);
+//   * logits S = Q K^T from fp32 MFMA 16x16x4 tiles: wave w takes slots
+//     16w..16w+15 of the chunk for every 16-head tile;
+//   * online softmax (base 2, scale folded in), four threads per head;
+//   * O += P V from fp32 MFMA tiles again, wave w owning the 16-column
+//     output tiles w, w+4, w+8, w+12.
+// A row split over several workgroups writes normalised partials and their
+// log-sum-exp; mla_f32_combine_kernel merges them.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void mla_f32_kernel(BatchDev bt, KeysDev kd, int heads, int d_qk,
-                                                     int d_v, const float *__restrict__ q,
-                                                     const float *__restrict__ kv,
-                                                     const int32_t *__restrict__ idx, int k,
-                                                     float sm_scale, float *__restrict__ out,
-                                                     float *__restrict__ lse) {
-  __shared__ float q_s[128];
-  __shared__ float p_s[64];
-  __shared__ int64_t row_s[64];
+constexpr int kF32MaxD = 256;
+constexpr int kF32Chunk = 64;
+constexpr int kF32Ld = kF32MaxD + 4;      // row stride in floats: 16 rows x 4 columns hit 64 banks
+constexpr int kF32PLd = kF32Chunk + 4;
+
+struct MlaF32Lds {
+  float q[64][kF32Ld];
+  float kv[kF32Chunk][kF32Ld];
+  float p[64][kF32PLd];
+  float alpha[64];
+  float l[64];
+  float m[64];
+  int64_t row[kF32Chunk];
+};
+
+__global__ __launch_bounds__(256) void mla_f32_kernel(BatchDev bt, KeysDev kd, int heads, int d_qk, int d_v,
+                                                      const float *__restrict__ q,
+                                                      const float *__restrict__ kv,
+                                                      const int32_t *__restrict__ idx, int k,
+                                                      int slots_per_split, int vec4, float sm_scale,
+                                                      float *__restrict__ out, float *__restrict__ lse,
+                                                      float *__restrict__ part_o,
+                                                      float *__restrict__ part_lse) {
+  __shared__ MlaF32Lds sh;
   const int t = blockIdx.x;
-  const int h = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int sp = blockIdx.y;
+  const int nsplit = gridDim.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = seq_of_row(bt, t);
-  const float *qh = q + ((int64_t)t * heads + h) * d_qk;
-  for (int d = lane; d < d_qk; d += 64) q_s[d] = qh[d];
-  __syncthreads();
-  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 64) {
-    const int j = j0 + lane;
-    const int s = j < k ? idx[(int64_t)t * k + j] : -1;
-    float z = -INFINITY;
-    int64_t row = -1;
-    if (s >= 0) {
-      row = key_row(kd, b, s);
-      const float *r = kv + row * d_qk;
-      float dot = 0.f;
-      for (int d = 0; d < d_qk; ++d) dot = fmaf(q_s[d], r[d], dot);
-      z = dot * sm_scale;
-    }
-    const float m_new = fmaxf(m, wave_max(z));
-    float p = 0.f, alpha = 1.f;
-    if (m_new != -INFINITY) {
-      p = s >= 0 ? expf(z - m_new) : 0.f;
-      alpha = expf(m - m_new);
-    }
-    float psum = p;
-    for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off, 64);
-    l = l * alpha + psum;
-    acc0 *= alpha;
-    acc1 *= alpha;
-    m = m_new;
-    p_s[lane] = p;
-    row_s[lane] = row;
-    __syncthreads();
-    const int cnt = min(64, k - j0);
-    for (int jj = 0; jj < cnt; ++jj) {
-      const int64_t r = row_s[jj];
-      if (r < 0) continue;
-      const float *v = kv + r * d_qk;
-      const float pj = p_s[jj];
-      if (lane < d_v) acc0 = fmaf(pj, v[lane], acc0);
-      if (lane + 64 < d_v) acc1 = fmaf(pj, v[lane + 64], acc1);
+  const int ht_n = (heads + 15) >> 4;          // 16-head tiles
+  const int hp = ht_n * 16;
+  const int nk = (d_qk + 3) >> 2;              // K steps of the logits
+  const int nt_n = (d_v + 15) >> 4;            // 16-column output tiles
+  const int s_begin = sp * slots_per_split;
+  const int s_end = min(k, s_begin + slots_per_split);
+  const int32_t *irow = idx + (int64_t)t * k;
+
+  // queries of every head, zero past d_qk and past the last head
+  const float *qt = q + (int64_t)t * heads * d_qk;
+  for (int h = wave; h < hp; h += 4)
+    for (int c = lane; c < kF32MaxD; c += 64) sh.q[h][c] = (h < heads && c < d_qk) ? qt[(int64_t)h * d_qk + c] : 0.f;
+
+  const float c2 = sm_scale * kLog2e;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  float m_run = -INFINITY, l_run = 0.f;        // of head tid >> 2 (four threads each)
+  v4f o[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) o[a][n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = s_begin; c0 < s_end; c0 += kF32Chunk) {
+    // slot -> row of the chunk (the previous chunk's P V is done in this wave;
+    // the barrier below makes it done in all before rows are overwritten)
+    if (tid < kF32Chunk) {
+      const int j = c0 + tid;
+      const int s = j < s_end ? irow[j] : -1;
+      sh.row[tid] = s >= 0 ? key_row(kd, b, s) : -1;
     }
     __syncthreads();
+    // gather: wave w fills rows 16w .. 16w+15 (float4 loads when rows are 16-byte aligned)
+    if (vec4) {
+#pragma unroll 4
+      for (int r = 16 * wave; r < 16 * wave + 16; ++r) {
+        const int64_t row = sh.row[r];
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row >= 0 && 4 * lane < d_qk) v = *(const float4 *)(kv + row * d_qk + 4 * lane);
+        *(float4 *)&sh.kv[r][4 * lane] = v;
+      }
+    } else {
+#pragma unroll 2
+      for (int r = 16 * wave; r < 16 * wave + 16; ++r) {
+        const int64_t row = sh.row[r];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = lane + 64 * u;
+          sh.kv[r][c] = (row >= 0 && c < d_qk) ? kv[row * d_qk + c] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    // logits of slots 16w .. 16w+15, in base-2 units, -inf where nothing is selected
+    const bool live = sh.row[16 * wave + r16] >= 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (a < ht_n) {
+        v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const float *qa = &sh.q[16 * a + r16][g4];
+        const float *kb = &sh.kv[16 * wave + r16][g4];
+        int ks = 0;
+        for (; ks + 1 < nk; ks += 2) {
+          s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * ks], kb[4 * ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * ks + 4], kb[4 * ks + 4], s1, 0, 0, 0);
+        }
+        if (ks < nk) s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * ks], kb[4 * ks], s0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sh.p[16 * a + 4 * g4 + i][16 * wave + r16] = live ? (s0[i] + s1[i]) * c2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax: head tid >> 2, slots 16 (tid & 3) .. +15 of the chunk
+    {
+      const int h = tid >> 2, qq = tid & 3;
+      if (h < hp) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)&sh.p[h][16 * qq + 4 * u];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx = fmaxf(fmaxf(fmaxf(mx, v[u].x), fmaxf(v[u].y, v[u].z)), v[u].w);
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        const float m_new = fmaxf(m_run, mx);
+        float alpha = 1.f, sum = 0.f;
+        if (m_new != -INFINITY) {
+          alpha = exp2f(m_run - m_new);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u].x = exp2f(v[u].x - m_new);
+            v[u].y = exp2f(v[u].y - m_new);
+            v[u].z = exp2f(v[u].z - m_new);
+            v[u].w = exp2f(v[u].w - m_new);
+            sum += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *(float4 *)&sh.p[h][16 * qq + 4 * u] = v[u];
+        if (qq == 0) sh.alpha[h] = alpha;
+      }
+    }
+    __syncthreads();
+    // O = alpha O + P V over the chunk's 64 slots
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (a < ht_n) {
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = sh.alpha[16 * a + 4 * g4 + i];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[a][n][i] *= al[i];
+        const float *pa = &sh.p[16 * a + r16][g4];
+#pragma unroll 4
+        for (int ks = 0; ks < kF32Chunk / 4; ++ks) {
+          const float av = pa[4 * ks];
+          const float *vb = &sh.kv[4 * ks + g4][r16];
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            if (wave + 4 * n < nt_n)
+              o[a][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, vb[16 * (wave + 4 * n)], o[a][n], 0, 0, 0);
+        }
+      }
+    }
   }
+
+  // totals of each head to LDS, then normalise and write
+  if ((tid & 3) == 0 && (tid >> 2) < hp) {
+    sh.l[tid >> 2] = l_run;
+    sh.m[tid >> 2] = m_run;
+  }
+  __syncthreads();
+  const bool split = nsplit > 1;
+  float *dst = split ? part_o + ((int64_t)t * nsplit + sp) * heads * d_v : out + (int64_t)t * heads * d_v;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    if (a < ht_n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * a + 4 * g4 + i;
+        if (h < heads) {
+          const float lh = sh.l[h];
+          const float inv = lh > 0.f ? 1.f / lh : 0.f;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const int d = 16 * (wave + 4 * n) + r16;
+            if (d < d_v) dst[(int64_t)h * d_v + d] = o[a][n][i] * inv;
+          }
+        }
+      }
+    }
+  }
+  if (tid < heads) {
+    const float lh = sh.l[tid];
+    const float v = lh > 0.f ? (sh.m[tid] + log2f(lh)) * kLn2 : -INFINITY;
+    if (split)
+      part_lse[((int64_t)t * nsplit + sp) * heads + tid] = v;
+    else if (lse)
+      lse[(int64_t)t * heads + tid] = v;
+  }
+}
+
+// Merges the fp32 partials of the nsplit ranges of each row: a wave per
+// (row, head), lanes over the output columns.
+__global__ __launch_bounds__(256) void mla_f32_combine_kernel(int heads, int d_v, int nsplit,
+                                                              const float *__restrict__ part_o,
+                                                              const float *__restrict__ part_lse,
+                                                              float *__restrict__ out,
+                                                              float *__restrict__ lse) {
+  const int t = blockIdx.x;
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= heads) return;
+  const float *pl = part_lse + (int64_t)t * nsplit * heads + h;
+  const float *po = part_o + ((int64_t)t * nsplit * heads + h) * d_v;
+  float mx = -INFINITY;
+  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * heads]);
+  float wsum = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
+    for (int i = 0; i < nsplit; ++i) {
+      const float li = pl[(int64_t)i * heads];
+      if (li == -INFINITY) continue;
+      const float w = expf(li - mx);
+      wsum += w;
+      const float *pi = po + (int64_t)i * heads * d_v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (lane + 64 * u < d_v) acc[u] = fmaf(w, pi[lane + 64 * u], acc[u]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float *o = out + ((int64_t)t * heads + h) * d_v;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (lane < d_v) o[lane] = acc0 * inv;
-  if (lane + 64 < d_v) o[lane + 64] = acc1 * inv;
-  if (lse && lane == 0) lse[(int64_t)t * heads + h] = l > 0.f ? m + logf(l) : -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (lane + 64 * u < d_v) o[lane + 64 * u] = acc[u] * inv;
+  if (lse && lane == 0) lse[(int64_t)t * heads + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 // --------------------------------------------------------------------------
@@ -445,13 +633,57 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int heads, int nsplit,
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
+// Ranges per fp32 row: enough workgroups to cover the CUs, at least one
+// 64-slot chunk each; ranges are whole chunks.
+static int mla_f32_chunks_per_split(int num_queries, int k) {
+  const int nch = (k + kF32Chunk - 1) / kF32Chunk;
+  int s = (256 + num_queries - 1) / num_queries;
+  if (s > nch) s = nch;
+  if (s < 1) s = 1;
+  return (nch + s - 1) / s;
+}
+
+int mla_f32_splits(int num_queries, int k) {
+  if (num_queries <= 0) return 1;
+  const int nch = (k + kF32Chunk - 1) / kF32Chunk;
+  const int per = mla_f32_chunks_per_split(num_queries, k);
+  return (nch + per - 1) / per;
+}
+
+size_t mla_f32_workspace_bytes(int num_queries, int heads, int d_v, int k) {
+  const int s = mla_f32_splits(num_queries, k);
+  if (s <= 1) return 0;
+  const size_t po = ((size_t)num_queries * s * heads * d_v * sizeof(float) + 15) / 16 * 16;
+  return po + (size_t)num_queries * s * heads * sizeof(float);
+}
+
+size_t mla_f32_workspace_bound(int num_queries, int heads, int d_v) {
+  if (num_queries <= 0) return 0;
+  const int s = (256 + num_queries - 1) / num_queries;  // no k gives more ranges than this
+  if (s <= 1) return 0;
+  const size_t po = ((size_t)num_queries * s * heads * d_v * sizeof(float) + 15) / 16 * 16;
+  return po + (size_t)num_queries * s * heads * sizeof(float);
+}
+
 hipError_t launch_mla_f32(const BatchDev &bt, const KeysDev &kd, int num_queries, int heads,
                           int d_qk, int d_v, const float *q, const float *kv,
                           const int32_t *indices, int k, float sm_scale, float *out, float *lse,
-                          hipStream_t stream) {
+                          void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_f32_kernel, dim3(num_queries, heads), dim3(64), 0, stream, bt, kd, heads,
-                     d_qk, d_v, q, kv, indices, k, sm_scale, out, lse);
+  const int per = mla_f32_chunks_per_split(num_queries, k);
+  const int nsplit = mla_f32_splits(num_queries, k);
+  float *part_o = nullptr, *part_lse = nullptr;
+  if (nsplit > 1) {
+    part_o = (float *)workspace;
+    part_lse = (float *)((char *)workspace +
+                         ((size_t)num_queries * nsplit * heads * d_v * sizeof(float) + 15) / 16 * 16);
+  }
+  hipLaunchKernelGGL(mla_f32_kernel, dim3(num_queries, nsplit), dim3(256), 0, stream, bt, kd, heads, d_qk,
+                     d_v, q, kv, indices, k, per * kF32Chunk, (int)(d_qk % 4 == 0 && (uintptr_t)kv % 16 == 0),
+                     sm_scale, out, lse, part_o, part_lse);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(mla_f32_combine_kernel, dim3(num_queries, (heads + 3) / 4), dim3(256), 0, stream, heads,
+                       d_v, nsplit, part_o, part_lse, out, lse);
   return hipGetLastError();
 }
 

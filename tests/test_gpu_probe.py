@@ -1,4 +1,4 @@
-"""Instruction-level probes on the GPU: the FP8 and bf16 MFMA operand and
+"""Instruction-level probes on the GPU: the FP8, bf16 and fp32 MFMA operand and
 accumulator lane layouts the kernels rely on (with them the OCP E4M3
 reading of FP8 bytes), and the lane map of the LDS transpose read."""
 
@@ -20,7 +20,8 @@ PROBE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def probe(gpu):
     lib = ctypes.CDLL(PROBE)
-    for name in ("dsa_probe_fp8_32x32x64", "dsa_probe_bf16_16x16x32", "dsa_probe_bf16_32x32x16"):
+    for name in ("dsa_probe_fp8_32x32x64", "dsa_probe_bf16_16x16x32", "dsa_probe_bf16_32x32x16",
+                 "dsa_probe_f32_16x16x4"):
         getattr(lib, name).argtypes = [ctypes.c_void_p] * 4
     lib.dsa_probe_tr16.argtypes = [ctypes.c_void_p] * 5
     return lib
@@ -144,6 +145,30 @@ def test_bf16_mfma_32x32x16_layout(probe, gpu):
     ref = At.double().numpy() @ Bt.double().numpy()
     assert not np.isnan(D).any()
     assert np.abs(D - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_f32_mfma_16x16x4_layout(probe, gpu):
+    """16x16x4 fp32: lane l holds A[l % 16, l // 16] and B[l // 16, l % 16];
+    accumulator register i of lane l holds row 4*(l//16) + i, column l % 16.
+    The products are fp32: against float64, four terms round like fp32."""
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((16, 4)).astype(np.float32)
+    Bm = rng.standard_normal((4, 16)).astype(np.float32)
+    a = np.array([A[l % 16, l // 16] for l in range(64)], np.float32)
+    b = np.array([Bm[l // 16, l % 16] for l in range(64)], np.float32)
+    da, db = torch.from_numpy(a).to(gpu), torch.from_numpy(b).to(gpu)
+    dd = torch.zeros((64, 4), dtype=torch.float32, device=gpu)
+    assert probe.dsa_probe_f32_16x16x4(da.data_ptr(), db.data_ptr(), dd.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    d = dd.cpu().numpy()
+    D = np.full((16, 16), np.nan)
+    for l in range(64):
+        for i in range(4):
+            D[4 * (l // 16) + i, l % 16] = d[l, i]
+    ref = A.astype(np.float64) @ Bm.astype(np.float64)
+    scale = np.abs(A.astype(np.float64)) @ np.abs(Bm.astype(np.float64))
+    assert not np.isnan(D).any()
+    assert (np.abs(D - ref) <= 4 * 2.0 ** -24 * scale).all()
 
 
 def test_lds_transpose_read_lane_map(probe, gpu):
