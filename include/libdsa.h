@@ -316,32 +316,38 @@ dsa_status_t dsa_output_projection_workspace_size(int32_t num_queries, int32_t h
  *               c = latent[b, s]
  *   out[b]   = concat_h o_h . w_out^T
  *
- * The page decompresses K and V per selected token; this computes the same
- * function with W_UK folded into the query and W_UV applied after the
- * softmax (hipBLASLt GEMMs, the fp32 indexer, top-k and sparse-MLA kernels).
- *   q_hidden [batch, hidden]; hist [batch, seq_len, hidden];
- *   latent [batch, seq_len, latent_dim] (<= 256); w_qi, w_ki [index_dim, hidden]
- *   (index_dim <= 128); w_q, w_uk, w_uv [heads * head_dim, hidden | latent_dim]
- *   (heads <= 64); w_out [hidden, heads * head_dim]; out [batch, hidden];
+ * The page projects every history row to k_I and decompresses K and V per
+ * selected token; this computes the same function with each weight folded
+ * into the side that has one vector per batch element: I[b, s] =
+ * ReLU(hist[b, s] . (w_ki^T q_I[b])) / sqrt(index_dim), W_UK folded into the
+ * query and W_UV applied after the softmax (matrix-vector kernels, the
+ * top-k and the fp32 sparse-MLA kernels; no GEMM library).
+ *   q_hidden [batch, hidden] (hidden <= 16384); hist [batch, seq_len, hidden];
+ *   latent [batch, seq_len, latent_dim] (<= 256); w_qi, w_ki [index_dim, hidden];
+ *   w_q, w_uk, w_uv [heads * head_dim, hidden | latent_dim] (heads <= 64);
+ *   w_out [hidden, heads * head_dim]; out [batch, hidden] (batch <= 65535);
  *   indices [batch, top_k] int32.  All fp32 except indices.
  *   workspace: 256-byte aligned, dsa_module_forward_workspace_size() bytes.
+ * Errors: DSA_ERR_INVALID_ARGUMENT (a size < 1, top_k outside [1, 65536], a
+ * NULL tensor, an unaligned workspace), DSA_ERR_UNSUPPORTED (limits above),
+ * DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP (a launch failed); nothing is
+ * enqueued when an argument is rejected.
  * ---------------------------------------------------------------------- */
-dsa_status_t dsa_module_forward(void *blaslt, int32_t batch, int32_t seq_len, int32_t hidden,
-                                int32_t heads, int32_t head_dim, int32_t latent_dim,
-                                int32_t index_dim, int32_t top_k, const float *q_hidden,
-                                const float *hist, const float *latent, const float *w_qi,
-                                const float *w_ki, const float *w_q, const float *w_uk,
-                                const float *w_uv, const float *w_out, float *out,
-                                int32_t *indices, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+dsa_status_t dsa_module_forward(int32_t batch, int32_t seq_len, int32_t hidden, int32_t heads,
+                                int32_t head_dim, int32_t latent_dim, int32_t index_dim,
+                                int32_t top_k, const float *q_hidden, const float *hist,
+                                const float *latent, const float *w_qi, const float *w_ki,
+                                const float *w_q, const float *w_uk, const float *w_uv,
+                                const float *w_out, float *out, int32_t *indices,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-dsa_status_t dsa_module_forward_workspace_size(int32_t batch, int32_t seq_len, int32_t heads,
-                                               int32_t head_dim, int32_t latent_dim,
-                                               int32_t index_dim, size_t *bytes);
+dsa_status_t dsa_module_forward_workspace_size(int32_t batch, int32_t seq_len, int32_t hidden,
+                                               int32_t heads, int32_t head_dim,
+                                               int32_t latent_dim, int32_t index_dim,
+                                               size_t *bytes);
 
-/* A hipBLASLt handle for dsa_output_projection and dsa_module_forward (host
- * and device resources of the GEMM library; the caller owns it and destroys
- * it). */
+/* A hipBLASLt handle for dsa_output_projection (host and device resources
+ * of the GEMM library; the caller owns it and destroys it). */
 dsa_status_t dsa_blaslt_create(void **handle);
 dsa_status_t dsa_blaslt_destroy(void *handle);
 

@@ -73,9 +73,10 @@ _SIGS = {
     "dsa_output_projection": [c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size,
                               c_ptr],
     "dsa_output_projection_workspace_size": [c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
-    "dsa_module_forward": [c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32] + [c_ptr] * 11
+    "dsa_module_forward": [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32] + [c_ptr] * 11
                           + [c_ptr, c_size, c_ptr],
-    "dsa_module_forward_workspace_size": [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
+    "dsa_module_forward_workspace_size": [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          ctypes.POINTER(c_size)],
     "dsa_blaslt_create": [ctypes.POINTER(c_ptr)],
     "dsa_blaslt_destroy": [c_ptr],
     "dsa_status_string": [c_i32],
@@ -276,18 +277,19 @@ def dsa_output_projection(blaslt, num_queries, heads, d_c, d_h, hidden, o, w_uv,
     return st
 
 
-def dsa_module_forward_workspace_size(batch, seq_len, heads, head_dim, latent_dim, index_dim):
+def dsa_module_forward_workspace_size(batch, seq_len, hidden, heads, head_dim, latent_dim, index_dim):
     n = c_size(0)
-    _check(lib().dsa_module_forward_workspace_size(int(batch), int(seq_len), int(heads), int(head_dim),
-                                                   int(latent_dim), int(index_dim), ctypes.byref(n)),
+    _check(lib().dsa_module_forward_workspace_size(int(batch), int(seq_len), int(hidden), int(heads),
+                                                   int(head_dim), int(latent_dim), int(index_dim),
+                                                   ctypes.byref(n)),
            "dsa_module_forward_workspace_size")
     return n.value
 
 
-def dsa_module_forward(blaslt, batch, seq_len, hidden, heads, head_dim, latent_dim, index_dim, top_k, q_hidden, hist,
+def dsa_module_forward(batch, seq_len, hidden, heads, head_dim, latent_dim, index_dim, top_k, q_hidden, hist,
                        latent, w_qi, w_ki, w_q, w_uk, w_uv, w_out, out, indices, workspace, workspace_bytes,
                        stream=None, check=True):
-    st = lib().dsa_module_forward(blaslt, int(batch), int(seq_len), int(hidden), int(heads), int(head_dim),
+    st = lib().dsa_module_forward(int(batch), int(seq_len), int(hidden), int(heads), int(head_dim),
                                   int(latent_dim), int(index_dim), int(top_k), _p(q_hidden), _p(hist), _p(latent),
                                   _p(w_qi), _p(w_ki), _p(w_q), _p(w_uk), _p(w_uv), _p(w_out), _p(out), _p(indices),
                                   _p(workspace), int(workspace_bytes), _stream(stream))

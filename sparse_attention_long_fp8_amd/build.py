@@ -25,7 +25,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "module.hip", "libdsa.cpp",
-               "projection.cpp"]
+               "projection.cpp", "module.cpp"]
 # the output projections are plain GEMMs, run by hipBLASLt
 LIB_LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 

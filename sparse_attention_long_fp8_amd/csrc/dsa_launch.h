@@ -61,4 +61,36 @@ hipError_t launch_cache_append(const KeysDev &kd, int num_tokens, const int32_t 
                                float *k_scale_pool, int d_c, const void *latent_new,
                                void *latent_pool, hipStream_t stream);
 
+// Matrix-vector products of the page-module entry point (fp32).
+// Row job: y[b * y_b_stride + r] = sum_c w[r * cols + c] * x[b * x_b_stride +
+// (r / rows_per_group) * x_g_stride + c] for r < rows; vec4 when cols and
+// both strides are multiples of 4 and w, x are 16-byte aligned.
+struct GemvRowJob {
+  const float *w;
+  const float *x;
+  float *y;
+  int rows, cols, rows_per_group, vec4;
+  int64_t x_b_stride, x_g_stride, y_b_stride;
+  int blocks;  // set by the launcher
+};
+// Column job: y[b * y_b_stride + g * y_g_stride + c] = sum_{j<J}
+// w[(g * J + j) * cols + c] * x[b * x_b_stride + g * x_g_stride + j].
+struct GemvColJob {
+  const float *w;
+  const float *x;
+  float *y;
+  int groups, J, cols;
+  int64_t x_b_stride, x_g_stride, y_b_stride, y_g_stride;
+  int blocks;  // set by the launcher
+};
+// Two independent jobs per launch (the second may have w == NULL).
+hipError_t launch_gemv_rows(GemvRowJob j0, GemvRowJob j1, int batch, hipStream_t stream);
+hipError_t launch_gemv_cols(GemvColJob j0, GemvColJob j1, int batch, hipStream_t stream);
+// scores[b * ld + s] = max(hist[b, s, :] . u[b, :], 0) * scale, s < S
+// (hidden <= 16384: u[b] is staged in LDS).
+hipError_t launch_module_scores(const float *hist, const float *u, int batch, int S, int hidden, float scale,
+                                float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_module_meta(int batch, int seq_len, int32_t *q_seq_start, int32_t *k_len,
+                              int64_t *k_seq_start, float *ones, hipStream_t stream);
+
 }  // namespace dsa

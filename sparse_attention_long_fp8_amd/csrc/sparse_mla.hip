@@ -75,9 +75,24 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(BatchDev bt, KeysDev kd, i
   const int32_t *irow = idx + (int64_t)t * k;
 
   // queries of every head, zero past d_qk and past the last head
+  // (each wave's 16 heads x 4 loads go out before the LDS stores)
   const float *qt = q + (int64_t)t * heads * d_qk;
-  for (int h = wave; h < hp; h += 4)
-    for (int c = lane; c < kF32MaxD; c += 64) sh.q[h][c] = (h < heads && c < d_qk) ? qt[(int64_t)h * d_qk + c] : 0.f;
+  {
+    float v[16][4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = wave + 4 * i;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = lane + 64 * u;
+        v[i][u] = (h < heads && c < d_qk) ? qt[(int64_t)h * d_qk + c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sh.q[wave + 4 * i][lane + 64 * u] = v[i][u];
+  }
 
   const float c2 = sm_scale * kLog2e;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -98,23 +113,34 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(BatchDev bt, KeysDev kd, i
     }
     __syncthreads();
     // gather: wave w fills rows 16w .. 16w+15 (float4 loads when rows are 16-byte aligned)
+    // (all 16 rows' loads are issued before the first LDS store)
     if (vec4) {
-#pragma unroll 4
-      for (int r = 16 * wave; r < 16 * wave + 16; ++r) {
-        const int64_t row = sh.row[r];
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row >= 0 && 4 * lane < d_qk) v = *(const float4 *)(kv + row * d_qk + 4 * lane);
-        *(float4 *)&sh.kv[r][4 * lane] = v;
-      }
-    } else {
-#pragma unroll 2
-      for (int r = 16 * wave; r < 16 * wave + 16; ++r) {
-        const int64_t row = sh.row[r];
+      float4 v[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = lane + 64 * u;
-          sh.kv[r][c] = (row >= 0 && c < d_qk) ? kv[row * d_qk + c] : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = sh.row[16 * wave + i];
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row >= 0 && 4 * lane < d_qk) v[i] = *(const float4 *)(kv + row * d_qk + 4 * lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *(float4 *)&sh.kv[16 * wave + i][4 * lane] = v[i];
+    } else {
+#pragma unroll
+      for (int h8 = 0; h8 < 16; h8 += 4) {
+        float v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = sh.row[16 * wave + h8 + i];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int c = lane + 64 * u;
+            v[i][u] = (row >= 0 && c < d_qk) ? kv[row * d_qk + c] : 0.f;
+          }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sh.kv[16 * wave + h8 + i][lane + 64 * u] = v[i][u];
       }
     }
     __syncthreads();
@@ -250,20 +276,43 @@ __global__ __launch_bounds__(256) void mla_f32_combine_kernel(int heads, int d_v
   if (h >= heads) return;
   const float *pl = part_lse + (int64_t)t * nsplit * heads + h;
   const float *po = part_o + ((int64_t)t * nsplit * heads + h) * d_v;
-  float mx = -INFINITY;
-  for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * heads]);
-  float wsum = 0.f;
+  // groups of 8 ranges: their lse and partial loads go out together, the
+  // weights follow from the running max
+  float mx = -INFINITY, wsum = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    for (int i = 0; i < nsplit; ++i) {
-      const float li = pl[(int64_t)i * heads];
-      if (li == -INFINITY) continue;
-      const float w = expf(li - mx);
-      wsum += w;
-      const float *pi = po + (int64_t)i * heads * d_v;
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {
+    float li[8], v[8][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (lane + 64 * u < d_v) acc[u] = fmaf(w, pi[lane + 64 * u], acc[u]);
+    for (int u = 0; u < 8; ++u) {
+      li[u] = -INFINITY;
+      const int i = i0 + u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[u][e] = 0.f;
+      if (i < nsplit) {
+        li[u] = pl[(int64_t)i * heads];
+        const float *pi = po + (int64_t)i * heads * d_v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (lane + 64 * e < d_v) v[u][e] = pi[lane + 64 * e];
+      }
+    }
+    float gm = mx;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, li[u]);
+    if (gm == -INFINITY) continue;  // nothing selected so far
+    const float c = mx == -INFINITY ? 0.f : expf(mx - gm);
+    wsum *= c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= c;
+    mx = gm;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (li[u] != -INFINITY) {
+        const float w = expf(li[u] - mx);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

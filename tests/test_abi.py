@@ -168,19 +168,20 @@ def test_cache_append_validation():
 
 def test_module_forward_validation():
     """Argument checks of dsa_module_forward run before anything is launched."""
-    nb = B.dsa_module_forward_workspace_size(2, 100, 4, 16, 64, 8)
+    nb = B.dsa_module_forward_workspace_size(2, 100, 64, 4, 16, 64, 8)
     ptrs = [0x100 * (i + 1) for i in range(11)]
 
-    def call(handle=0x1, sizes=(2, 100, 64, 4, 16, 64, 8, 32), ptr=ptrs, ws=0x10000, nbytes=nb):
-        return B.dsa_module_forward(handle, *sizes, *ptr, ws, nbytes, check=False)
+    def call(sizes=(2, 100, 64, 4, 16, 64, 8, 32), ptr=ptrs, ws=0x10000, nbytes=nb):
+        return B.dsa_module_forward(*sizes, *ptr, ws, nbytes, check=False)
 
-    assert call(handle=None) == B.DSA_ERR_INVALID_ARGUMENT
     assert call(sizes=(2, 0, 64, 4, 16, 64, 8, 32)) == B.DSA_ERR_INVALID_ARGUMENT
     assert call(sizes=(2, 100, 64, 65, 16, 64, 8, 32)) == B.DSA_ERR_UNSUPPORTED    # > 64 heads
     assert call(sizes=(2, 100, 64, 4, 16, 257, 8, 32)) == B.DSA_ERR_UNSUPPORTED    # latent > 256
+    assert call(sizes=(2, 100, 16385, 4, 16, 64, 8, 32)) == B.DSA_ERR_UNSUPPORTED  # hidden > 16384
+    assert call(sizes=(65536, 4, 64, 4, 16, 64, 8, 32)) == B.DSA_ERR_UNSUPPORTED   # batch > 65535
     assert call(sizes=(2, 100, 64, 4, 16, 64, 8, 0)) == B.DSA_ERR_INVALID_ARGUMENT
-    assert call(sizes=(65536, 65536, 64, 4, 16, 64, 8, 32)) == B.DSA_ERR_UNSUPPORTED
+    assert call(sizes=(32768, 65536, 64, 4, 16, 64, 8, 32)) == B.DSA_ERR_UNSUPPORTED
     assert call(ptr=ptrs[:5] + [0] + ptrs[6:]) == B.DSA_ERR_INVALID_ARGUMENT
     assert call(nbytes=nb - 1) == B.DSA_ERR_WORKSPACE_TOO_SMALL
     assert call(ws=0x10010) == B.DSA_ERR_INVALID_ARGUMENT                          # not 256-byte aligned
-    assert B.lib().dsa_module_forward_workspace_size(2, 100, 4, 16, 64, 8, None) == B.DSA_ERR_INVALID_ARGUMENT
+    assert B.lib().dsa_module_forward_workspace_size(2, 100, 64, 4, 16, 64, 8, None) == B.DSA_ERR_INVALID_ARGUMENT

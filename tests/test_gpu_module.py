@@ -25,13 +25,6 @@ TOL = 1e-4
 TIE_RTOL = 1e-3
 
 
-@pytest.fixture(scope="module")
-def blaslt(gpu):
-    h = B.dsa_blaslt_create()
-    yield h
-    B.dsa_blaslt_destroy(h)
-
-
 def _lin(rng, out_f, in_f):
     b = 1.0 / np.sqrt(in_f)
     return rng.uniform(-b, b, (out_f, in_f)).astype(np.float32)
@@ -42,7 +35,7 @@ def _lin(rng, out_f, in_f):
     (3, 300, 256, 4, 32, 128, 16, 512),       # top_k > history: every key kept, -1 padding
     (1, 2000, 128, 8, 16, 64, 8, 64),
 ])
-def test_module_forward_matches_oracle(gpu, blaslt, Bn, S, hidden, H, d_h, d_c, d_i, top_k):
+def test_module_forward_matches_oracle(gpu, Bn, S, hidden, H, d_h, d_c, d_i, top_k):
     rng = np.random.default_rng(S + H)
     qh = rng.standard_normal((Bn, hidden)).astype(np.float32)
     hist = rng.standard_normal((Bn, S, hidden)).astype(np.float32)
@@ -52,10 +45,10 @@ def test_module_forward_matches_oracle(gpu, blaslt, Bn, S, hidden, H, d_h, d_c, 
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
     out = torch.full((Bn, hidden), float("nan"), device=gpu)
     idx = torch.full((Bn, top_k), -7, dtype=torch.int32, device=gpu)
-    nb = B.dsa_module_forward_workspace_size(Bn, S, H, d_h, d_c, d_i)
+    nb = B.dsa_module_forward_workspace_size(Bn, S, hidden, H, d_h, d_c, d_i)
     ws = torch.empty(nb + 256, dtype=torch.uint8, device=gpu)
     base = ws.data_ptr() + (-ws.data_ptr()) % 256
-    B.dsa_module_forward(blaslt, Bn, S, hidden, H, d_h, d_c, d_i, top_k, t(qh), t(hist), t(lat), *[t(w) for w in W],
+    B.dsa_module_forward(Bn, S, hidden, H, d_h, d_c, d_i, top_k, t(qh), t(hist), t(lat), *[t(w) for w in W],
                          out, idx, base, nb)
     torch.cuda.synchronize()
     got_out, got_idx = out.cpu().numpy().astype(np.float64), idx.cpu().numpy()
