@@ -184,6 +184,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   };
 
   // ---- 2. histogram, threshold bin ----
+  // The lowest bin takes the row minimum with all its duplicates (the exact
+  // zeros of ReLU scores): each thread counts those in a register and adds
+  // them once, instead of every thread hitting one LDS counter per element.
+  uint32_t low = 0u;
   for (int base = 0; base < n; base += kChunk) {
     float4 v[kU];
     DSA_SWEEP_CHUNK(base, v);
@@ -192,10 +196,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
       const int i = base + 4 * (tid + u * kTkThreads);
       const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i + j < n) atomicAdd(&sh.hist[bin_of(f[j])], 1u);
+      for (int j = 0; j < 4; ++j) {
+        if (i + j < n) {
+          const int bn = bin_of(f[j]);
+          if (bn == 0)
+            ++low;
+          else
+            atomicAdd(&sh.hist[bn], 1u);
+        }
+      }
     }
   }
+  if (low) atomicAdd(&sh.hist[0], low);
   lds_barrier();
   if (wave == 0) scan_from_top(sh.hist, kTkBins, k, &sh.scan_bin, &sh.scan_above);
   lds_barrier();
@@ -307,9 +319,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
       const int R = ((np + kTkThreads - 1) / kTkThreads + 3) & ~3;
       const int r0 = p0 + tid * R;
       uint32_t gtm = 0u, eqm = 0u;
-      for (int q = 0; q < R / 4; ++q) {
-        // rotated order (q + tid) % (R/4): neighbouring lanes hit different LDS banks
-        const int qq = (q + tid) % (R / 4);
+      // Rotated read order.  When R divides 64, 64/R runs share a 256-byte
+      // row of the 64 LDS banks and run tid starts at tid*R/64: 16
+      // neighbouring lanes then read 16 different 16-byte bank groups (a
+      // rotation by tid alone maps lanes l and l+8, at R = 32, or all 16
+      // lanes, at R = 16, to one group).  Other run lengths rotate by tid.
+      const int r4 = R / 4;
+      const int rot = (64 % R == 0 ? (tid * R) >> 6 : tid) % r4;
+      for (int q = 0; q < r4; ++q) {
+        const int qq = q + rot < r4 ? q + rot : q + rot - r4;
         const int i = r0 + 4 * qq;
         if (i >= p0 + np) continue;
         const float4 v = *(const float4 *)(&sh.cache[i]);

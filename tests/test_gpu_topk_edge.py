@@ -1,8 +1,9 @@
 """Top-k on crafted score rows, bit-exact against the oracle's selection:
 heavy ties (small bins resolved by ranking, large ones by radix digits), a
 constant row (the whole row is one bin, past the candidate list), signed
-zeros, all-negative rows, rows longer than the LDS row cache, and rows
-shorter than k.  Each row is its own sequence, so n_t = k_len[t]; entries
+zeros, all-negative rows, rows longer than the LDS row cache, rows
+shorter than k, ReLU rows that are half exact zeros, and k above the 2048
+outputs assembled in LDS.  Each row is its own sequence, so n_t = k_len[t]; entries
 past n_t are NaN and must never be read."""
 
 import zlib
@@ -31,13 +32,17 @@ def _rows(kind, rng):
         return [-rng.random(9000).astype(np.float32) - 1.0 for _ in range(2)], 512
     if kind == "long_rows":
         return [rng.integers(0, 1000, 70000).astype(np.float32), rng.standard_normal(100000).astype(np.float32)], 2048
+    if kind == "relu_zeros":   # about half the row is exactly 0 (one histogram bin)
+        return [np.maximum(rng.standard_normal(16384), 0).astype(np.float32) for _ in range(2)], 512
+    if kind == "k_above_staging":   # more outputs than the LDS staging holds: direct stores
+        return [rng.standard_normal(20000).astype(np.float32), rng.integers(0, 50, 40000).astype(np.float32)], 3000
     if kind == "short_rows":
         return [rng.standard_normal(n).astype(np.float32) for n in (1, 10, 63, 64, 65)], 64
     raise KeyError(kind)
 
 
 @pytest.mark.parametrize("kind", ["ties_small_bins", "ties_few_values", "constant", "signed_zero",
-                                  "all_negative", "long_rows", "short_rows"])
+                                  "all_negative", "long_rows", "short_rows", "relu_zeros", "k_above_staging"])
 def test_topk_crafted_rows(kind, gpu):
     print("\n[topk-edge] %s" % kind, flush=True)
     rng = np.random.default_rng(zlib.crc32(kind.encode()))
