@@ -218,8 +218,49 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   if (tid == 0) sh.cand_count = 0;
   lds_barrier();
 
+  // A cached row (n <= 32768) is one piece: thread tid owns the contiguous
+  // run [tid*R, tid*R + R), R <= 32 a multiple of 4.  Rotated read order:
+  // when R divides 64, 64/R runs share a 256-byte row of the 64 LDS banks
+  // and run tid starts at tid*R/64, so 16 neighbouring lanes read 16
+  // different 16-byte bank groups (a rotation by tid alone maps lanes l and
+  // l+8, at R = 32, or all 16 lanes, at R = 16, to one group).  Other run
+  // lengths rotate by tid.
+  const int R = ((min(n, kChunk) + kTkThreads - 1) / kTkThreads + 3) & ~3;
+  const int r0 = tid * R;
+  const int r4 = R / 4;
+  const int rot = (64 % R == 0 ? (tid * R) >> 6 : tid) % r4;
+  // When the row is cached and bin b* fits the candidate list, the list is
+  // built from the runs, and each thread keeps bitmasks of its elements in
+  // bins above b* (all above tau: the binning is monotone) and in b*; the
+  // ordered pass then re-tests only the in-bin elements against tau.
+  const bool run_masks = cached && use_list;
+  uint32_t above_bin = 0u, in_bin = 0u;
+
   // ---- 3. exact threshold inside bin b* ----
-  if (use_list) {
+  if (run_masks) {
+    for (int q = 0; q < r4; ++q) {
+      const int qq = q + rot < r4 ? q + rot : q + rot - r4;
+      const int i = r0 + 4 * qq;
+      if (i >= n) continue;
+      const float4 v = *(const float4 *)(&sh.cache[i]);
+      const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i + j >= n) break;
+        const int bn = bin_of(f[j]);
+        above_bin |= (uint32_t)(bn > bstar) << (4 * qq + j);
+        if (bn == bstar) {
+          in_bin |= 1u << (4 * qq + j);
+          const int slot = atomicAdd(&sh.cand_count, 1);
+          if (slot < kTkCand) {
+            sh.cand[slot] = i + j;
+            sh.cand_key[slot] = float_key(f[j]);
+          }
+        }
+      }
+    }
+    lds_barrier();
+  } else if (use_list) {
     for (int base = 0; base < n; base += kChunk) {
       float4 v[kU];
       DSA_SWEEP_CHUNK(base, v);
@@ -309,46 +350,49 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
   int gt_run = 0, eq_run = 0;
   if (cached) {
-    // The row is in LDS.  Thread i owns the contiguous run [i*R, i*R + R)
-    // (R <= 32, a multiple of 4) and keeps bitmasks of its elements above and
-    // equal to tau; one block-wide exclusive scan of the two counts gives
-    // every run its output offset, so the output comes out ascending without
-    // any per-element synchronisation.
-    for (int p0 = 0; p0 < n; p0 += kChunk) {
-      const int np = min(n - p0, kChunk);
-      const int R = ((np + kTkThreads - 1) / kTkThreads + 3) & ~3;
-      const int r0 = p0 + tid * R;
+    // The row is in LDS, one piece of runs (above).  Each thread holds
+    // bitmasks of its run's elements above and equal to tau; one block-wide
+    // exclusive scan of the two counts gives every run its output offset, so
+    // the output comes out ascending without any per-element synchronisation.
+    {
       uint32_t gtm = 0u, eqm = 0u;
-      // Rotated read order.  When R divides 64, 64/R runs share a 256-byte
-      // row of the 64 LDS banks and run tid starts at tid*R/64: 16
-      // neighbouring lanes then read 16 different 16-byte bank groups (a
-      // rotation by tid alone maps lanes l and l+8, at R = 32, or all 16
-      // lanes, at R = 16, to one group).  Other run lengths rotate by tid.
-      const int r4 = R / 4;
-      const int rot = (64 % R == 0 ? (tid * R) >> 6 : tid) % r4;
-      for (int q = 0; q < r4; ++q) {
-        const int qq = q + rot < r4 ? q + rot : q + rot - r4;
-        const int i = r0 + 4 * qq;
-        if (i >= p0 + np) continue;
-        const float4 v = *(const float4 *)(&sh.cache[i]);
-        const float f[4] = {v.x, v.y, v.z, v.w};
+      if (run_masks) {
+        gtm = above_bin;
+        for (uint32_t m = in_bin; m; m &= m - 1) {
+          const int bit = __ffs(m) - 1;
+          const uint32_t key = float_key(sh.cache[r0 + bit]);
+          gtm |= (uint32_t)(key > tau) << bit;
+          eqm |= (uint32_t)(key == tau) << bit;
+        }
+      } else {
+        for (int q = 0; q < r4; ++q) {
+          const int qq = q + rot < r4 ? q + rot : q + rot - r4;
+          const int i = r0 + 4 * qq;
+          if (i >= n) continue;
+          const float4 v = *(const float4 *)(&sh.cache[i]);
+          const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (i + j >= p0 + np) break;
-          const uint32_t key = float_key(f[j]);
-          gtm |= (uint32_t)(key > tau) << (4 * qq + j);
-          eqm |= (uint32_t)(key == tau) << (4 * qq + j);
+          for (int j = 0; j < 4; ++j) {
+            if (i + j >= n) break;
+            const uint32_t key = float_key(f[j]);
+            gtm |= (uint32_t)(key > tau) << (4 * qq + j);
+            eqm |= (uint32_t)(key == tau) << (4 * qq + j);
+          }
         }
       }
       const int gc = __popc(gtm), ec = __popc(eqm);
-      // block-wide exclusive scan of (gc, ec): lanes, then waves
-      int gi = gc, ei = ec;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int yg = __shfl_up(gi, off, 64);
-        const int ye = __shfl_up(ei, off, 64);
-        if (lane >= off) { gi += yg; ei += ye; }
+      // block-wide exclusive scan of (gc, ec) <= 32: lanes by bit-plane
+      // ballots (six planes each), then waves through LDS
+      int gi = 0, ei = 0, gwave = 0, ewave = 0;
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const uint64_t bg = __ballot((gc >> bit) & 1), be = __ballot((ec >> bit) & 1);
+        gi += lanes_below(bg) << bit;
+        ei += lanes_below(be) << bit;
+        gwave += __popcll(bg) << bit;
+        ewave += __popcll(be) << bit;
       }
-      if (lane == 63) { sh.cnt[0][0][wave] = gi; sh.cnt[0][1][wave] = ei; }
+      if (lane == 0) { sh.cnt[0][0][wave] = gwave; sh.cnt[0][1][wave] = ewave; }
       lds_barrier();
       int gw = 0, ew = 0, gb = 0, eb = 0;
       for (int w2 = 0; w2 < kTkWaves; ++w2) {
@@ -357,8 +401,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
         gb += gv;
         eb += ev;
       }
-      int g_before = gt_run + gw + gi - gc;
-      int e_before = eq_run + ew + ei - ec;
+      int g_before = gt_run + gw + gi;
+      int e_before = eq_run + ew + ei;
       uint32_t m = gtm | eqm;
       while (m) {
         const int bit = __ffs(m) - 1;
@@ -378,7 +422,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
       }
       gt_run += gb;
       eq_run += eb;
-      lds_barrier();  // sh.cnt is reused by the next piece
     }
   } else {
     // The row is read in pieces of 32768 elements (the first from LDS), each
