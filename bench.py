@@ -556,6 +556,18 @@ def main():
         rooflines[st_name]["kernel"] = kernel_name(st_name, wl, lay)
         rooflines[st_name]["us"] = stage_ms[st_name] * 1e3
     dominant = max(stage_ms, key=stage_ms.get)
+    # The path's own fraction over indexer + attention, top-k reported apart
+    # (the stage-by-stage loop's times): decode, algorithmic bytes of both
+    # against HBM; prefill, both stages' flops each at its own dtype's peak.
+    t_path = (stage_ms["indexer"] + stage_ms["mla"]) / 1e3
+    if decode:
+        path = {"bound": "hbm", "frac": (work["indexer"]["bytes"] + work["mla"]["bytes"]) / HBM_PEAK / t_path,
+                "definition": "(indexer bytes + attention bytes) / (8 TB/s x (t_indexer + t_attention))"}
+    else:
+        path = {"bound": "mfma", "frac": (work["indexer"]["flops"] / work["indexer"]["peak_flops"]
+                                          + work["mla"]["flops"] / work["mla"]["peak_flops"]) / t_path,
+                "definition": "(indexer flops / its peak + attention flops / its peak) / (t_indexer + t_attention)"}
+    path["us"] = t_path * 1e6
     result = {
         "metric": METRIC,
         "value": T / (ms_step / 1e3),
@@ -576,6 +588,7 @@ def main():
         "decode_us_per_step": ms_step * 1e3 if decode else None,
         "roofline": dict(rooflines[dominant]),
         "stages": rooflines,
+        "path_roofline": path,
     }
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (budget %.0f s)" % args.cpu_budget, file=sys.stderr, flush=True)

@@ -352,6 +352,45 @@ dsa_status_t dsa_blaslt_create(void **handle);
 dsa_status_t dsa_blaslt_destroy(void *handle);
 
 /* ------------------------------------------------------------------------
+ * Precondition check on request.  The entry points above validate their
+ * arguments on the host but document, without testing while they run, the
+ * preconditions on device data (one read of each would cost a launch-wide
+ * pass).  dsa_validate tests them on the stream, reading only, and writes
+ * the first violation it finds to `report` (4 device int32):
+ *   report[0] = dsa_check_code_t (0: none found);
+ *   report[1..3] = where, by code:
+ *     DSA_CHECK_BATCH     sequence b, its query count, k_len[b]: q_seq_start
+ *                         must start at 0, not decrease, end at num_queries,
+ *                         with every count <= max_q_per_seq and
+ *                         count <= k_len[b] <= max_k_len;
+ *     DSA_CHECK_ROWS      sequence b, k_len[b], k_seq_start[b]: a contiguous
+ *                         sequence's rows must lie in [0, num_rows);
+ *     DSA_CHECK_PAGE      sequence b, page index p, page id: every page a
+ *                         sequence uses must be in [0, num_rows(pages));
+ *     DSA_CHECK_INDEX     row t, slot j, value: indices must be -1 or in
+ *                         [0, n_t) (dsa_sparse_mla_fwd's input);
+ *     DSA_CHECK_NAN_SCORE row t, position s, 0: scores[t, s < n_t] must not be
+ *                         NaN (dsa_topk's input).
+ * The batch and layout checks always run (layout may be NULL: no row or page
+ * checks); `indices` (with k) and `scores` (with ld_scores >= max_k_len) are
+ * optional.  Host-side argument errors return as elsewhere and enqueue
+ * nothing.  The report is valid once the stream reaches this call's end; the
+ * caller reads it back.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  DSA_CHECK_OK = 0,
+  DSA_CHECK_BATCH = 1,
+  DSA_CHECK_ROWS = 2,
+  DSA_CHECK_PAGE = 3,
+  DSA_CHECK_INDEX = 4,
+  DSA_CHECK_NAN_SCORE = 5
+} dsa_check_code_t;
+
+dsa_status_t dsa_validate(const dsa_batch_t *batch, const dsa_kv_layout_t *layout,
+                          const int32_t *indices, int32_t k, const float *scores,
+                          int64_t ld_scores, int32_t *report, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ---------------------------------------------------------------------- */
 const char *dsa_status_string(dsa_status_t status);   /* static string */

@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "libdsa.h")
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = range(3)
+DSA_CHECK_OK, DSA_CHECK_BATCH, DSA_CHECK_ROWS, DSA_CHECK_PAGE, DSA_CHECK_INDEX, DSA_CHECK_NAN_SCORE = range(6)
 
 c_i32, c_i64, c_f32, c_ptr, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -57,6 +58,8 @@ _SIGS = {
     "dsa_indexer_scores": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32, c_i32,
                            c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_f32, c_ptr, c_i64, c_ptr],
     "dsa_topk": [ctypes.POINTER(dsa_batch_t), c_ptr, c_i64, c_i32, c_ptr, c_ptr, c_size, c_ptr],
+    "dsa_validate": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_ptr, c_i32, c_ptr, c_i64, c_ptr,
+                     c_ptr],
     "dsa_topk_workspace_size": [ctypes.POINTER(dsa_batch_t), c_i32, ctypes.POINTER(c_size)],
     "dsa_sparse_mla_fwd": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32, c_i32,
                            c_i32, c_ptr, c_ptr, c_ptr, c_i32, c_f32, c_ptr, c_ptr, c_ptr, c_size, c_ptr],
@@ -182,6 +185,15 @@ def dsa_topk_workspace_size(batch, k):
     n = c_size(0)
     _check(lib().dsa_topk_workspace_size(ctypes.byref(batch), int(k), ctypes.byref(n)), "dsa_topk_workspace_size")
     return n.value
+
+
+def dsa_validate(batch, layout, indices, k, scores, ld_scores, report, stream=None, check=True):
+    """Enqueue the precondition checks; `report` is a device int32[4] (see libdsa.h)."""
+    st = lib().dsa_validate(ctypes.byref(batch), None if layout is None else ctypes.byref(layout), _p(indices),
+                            int(k), _p(scores), int(ld_scores), _p(report), _stream(stream))
+    if check:
+        _check(st, "dsa_validate")
+    return st
 
 
 def dsa_topk(batch, scores, ld_scores, k, indices, workspace=None, workspace_bytes=0, stream=None, check=True):

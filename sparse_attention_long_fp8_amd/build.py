@@ -24,8 +24,8 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
-LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "module.hip", "libdsa.cpp",
-               "projection.cpp", "module.cpp"]
+LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "module.hip", "validate.hip",
+               "libdsa.cpp", "projection.cpp", "module.cpp"]
 # the output projections are plain GEMMs, run by hipBLASLt
 LIB_LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -61,6 +61,25 @@ hipError_t launch_cache_append(const KeysDev &kd, int num_tokens, const int32_t 
                                float *k_scale_pool, int d_c, const void *latent_new,
                                void *latent_pool, hipStream_t stream);
 
+// On-request precondition checks (dsa_validate).  Codes match
+// dsa_check_code_t in libdsa.h.
+enum { kCheckBatch = 1, kCheckRows = 2, kCheckPage = 3, kCheckIndex = 4, kCheckNanScore = 5 };
+struct ValidateArgs {
+  int32_t num_seqs, num_queries, max_q_per_seq, max_k_len;
+  const int32_t *q_seq_start, *k_len;  // NULL (empty batch): only the report is cleared
+  int32_t has_layout;                  // 0: no row or page checks
+  int32_t paged;
+  const int64_t *k_seq_start;
+  const int32_t *page_table;
+  int32_t page_table_stride;
+  int64_t num_rows;
+  const int32_t *indices;  // [T, k] or NULL
+  int32_t k;
+  const float *scores;     // [T, ld] or NULL
+  int64_t ld;
+};
+hipError_t launch_validate(const ValidateArgs &a, int32_t *report, hipStream_t stream);
+
 // Matrix-vector products of the page-module entry point (fp32).
 // Row job: y[b * y_b_stride + r] = sum_c w[r * cols + c] * x[b * x_b_stride +
 // (r / rows_per_group) * x_g_stride + c] for r < rows; vec4 when cols and

@@ -255,6 +255,41 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
   return ok();
 }
 
+dsa_status_t dsa_validate(const dsa_batch_t *batch, const dsa_kv_layout_t *layout, const int32_t *indices,
+                          int32_t k, const float *scores, int64_t ld_scores, int32_t *report, hipStream_t stream) {
+  dsa_status_t st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (layout && (st = check_layout(layout, batch, "key")) != DSA_OK) return st;
+  if (!report) return fail(DSA_ERR_INVALID_ARGUMENT, "validate: report is NULL");
+  if (!aligned(report, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "validate: report must be 4-byte aligned");
+  if (indices && (k < 1 || k > 65536)) return fail(DSA_ERR_INVALID_ARGUMENT, "validate: k must be in [1, 65536]");
+  if (scores && ld_scores < batch->max_k_len)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "validate: ld_scores %lld < max_k_len %d", (long long)ld_scores,
+                batch->max_k_len);
+  if (batch->num_queries > 0 && (!batch->q_seq_start || !batch->k_len))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "validate: q_seq_start / k_len is NULL");
+  dsa::ValidateArgs a{};
+  a.num_seqs = batch->num_seqs;
+  a.num_queries = batch->num_queries;
+  a.max_q_per_seq = batch->max_q_per_seq;
+  a.max_k_len = batch->max_k_len;
+  a.q_seq_start = batch->q_seq_start;
+  a.k_len = batch->k_len;
+  a.has_layout = layout != nullptr;
+  if (layout) {
+    a.paged = layout->paged;
+    a.k_seq_start = layout->k_seq_start;
+    a.page_table = layout->page_table;
+    a.page_table_stride = layout->page_table_stride;
+    a.num_rows = layout->num_rows;
+  }
+  a.indices = indices;
+  a.k = indices ? k : 0;
+  a.scores = scores;
+  a.ld = ld_scores;
+  return hip_status(dsa::launch_validate(a, report, stream), "validate launch");
+}
+
 dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_scores, int32_t k, int32_t *indices,
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
   (void)workspace;

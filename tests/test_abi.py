@@ -21,7 +21,7 @@ def _layout(rows=8):
 def test_exports_match_header():
     lib = B.lib()
     names = B.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
 
@@ -185,3 +185,16 @@ def test_module_forward_validation():
     assert call(nbytes=nb - 1) == B.DSA_ERR_WORKSPACE_TOO_SMALL
     assert call(ws=0x10010) == B.DSA_ERR_INVALID_ARGUMENT                          # not 256-byte aligned
     assert B.lib().dsa_module_forward_workspace_size(2, 100, 64, 4, 16, 64, 8, None) == B.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_validate_argument_errors():
+    """dsa_validate's host-side checks; nothing is launched on these."""
+    bt, ly = _batch(), _layout()
+    assert B.dsa_validate(bt, ly, None, 0, None, 0, None, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # no report
+    assert B.dsa_validate(bt, ly, None, 0, None, 0, 0x102, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # unaligned
+    assert B.dsa_validate(bt, ly, 0x400, 0, None, 0, 0x100, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # k < 1
+    assert B.dsa_validate(bt, ly, None, 0, 0x500, 7, 0x100, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # ld < max_k
+    paged = B.dsa_kv_layout_t(1, None, 0x3000, 4, 32, 8)
+    assert B.dsa_validate(bt, paged, None, 0, None, 0, 0x100, check=False) == B.DSA_ERR_UNSUPPORTED   # page size
+    bad = B.dsa_batch_t(0, 4, 0x1000, 0x2000, 4, 8)
+    assert B.dsa_validate(bad, ly, None, 0, None, 0, 0x100, check=False) == B.DSA_ERR_INVALID_ARGUMENT
