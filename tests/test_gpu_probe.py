@@ -185,9 +185,5 @@ def test_lds_transpose_read_lane_map(probe, gpu):
     assert st == 0
     torch.cuda.synchronize()
     got = dst.cpu().numpy()
-    os.makedirs("gpurun_out", exist_ok=True)
-    with open("gpurun_out/tr16_lane_map.txt", "w") as f:
-        for l in range(64):
-            f.write("%2d: %s\n" % (l, " ".join("%4d" % v for v in got[l])))
     want = np.array([[64 * (l // 16) + 16 * r + l % 16 for r in range(4)] for l in range(64)])
     assert np.array_equal(got, want)
