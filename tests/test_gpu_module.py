@@ -34,6 +34,8 @@ def _lin(rng, out_f, in_f):
     (2, 16384, 1024, 16, 64, 256, 32, 512),   # the page's verification shape
     (3, 300, 256, 4, 32, 128, 16, 512),       # top_k > history: every key kept, -1 padding
     (1, 2000, 128, 8, 16, 64, 8, 64),
+    (6, 700, 256, 4, 32, 128, 16, 100),       # batch > 4: a second pass of every matrix-vector kernel
+    (5, 333, 130, 3, 10, 50, 7, 96),          # widths not multiples of 4: the scalar paths throughout
 ])
 def test_module_forward_matches_oracle(gpu, Bn, S, hidden, H, d_h, d_c, d_i, top_k):
     rng = np.random.default_rng(S + H)
