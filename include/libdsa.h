@@ -133,7 +133,12 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t *batch, const dsa_kv_layout_t 
  * slots.  Ties go to the lowest position; scores compare by value (-0 == +0).
  * NaN scores are a precondition violation (the result is then unspecified
  * but stays in range).  The result is deterministic.
- *   1 <= k <= 65536.  workspace: dsa_topk_workspace_size() bytes (may be 0).
+ *   1 <= k <= 65536.  workspace: dsa_topk_workspace_size() bytes, 256-byte
+ *   aligned: nonzero for batches of fewer than 256 rows with histories past
+ *   32768, which are selected in two passes (each 32768-long part of a row,
+ *   then the union of the parts' winners) through per-row candidate lists
+ *   of at most max_k_len positions and scores; 0 otherwise.
+ *   DSA_ERR_WORKSPACE_TOO_SMALL if it is short.
  * ---------------------------------------------------------------------- */
 dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_scores,
                       int32_t k, int32_t *indices,

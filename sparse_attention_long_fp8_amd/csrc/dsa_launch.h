@@ -32,8 +32,11 @@ hipError_t launch_indexer_topk_fused(const BatchDev &bt, const int64_t *k_seq_st
                                      const float *k_scale, float scale, int topk, int32_t *indices,
                                      void *workspace, hipStream_t stream);
 
-hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
-                       int k, int32_t *indices, hipStream_t stream);
+// Top-k; batches of few rows with histories past the LDS row cache use a
+// workspace of topk_workspace_bytes (0 otherwise).
+size_t topk_workspace_bytes(int num_queries, int max_k_len, int k);
+hipError_t launch_topk(const BatchDev &bt, int num_queries, int max_k_len, const float *scores, int64_t ld,
+                       int k, int32_t *indices, void *workspace, hipStream_t stream);
 
 // Split count the bf16 sparse-MLA kernel uses for this many query rows
 // (1 = no split, no workspace).

@@ -160,7 +160,8 @@ bool fused_applies(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t
 size_t indexer_topk_ws(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i, int32_t d_i,
                        int32_t k) {
   if (fused_applies(bt, ly, dt, h_i, d_i)) return dsa::fused_topk_workspace_bytes(bt->num_queries, k);
-  return round_up((size_t)bt->num_queries * round_up((size_t)bt->max_k_len, 4) * sizeof(float), 256);
+  return round_up((size_t)bt->num_queries * round_up((size_t)bt->max_k_len, 4) * sizeof(float), 256) +
+         dsa::topk_workspace_bytes(bt->num_queries, bt->max_k_len, k);
 }
 
 // Workspace carve-up of dsa_forward: [scores or fused candidate lists][indices][mla partials],
@@ -169,7 +170,7 @@ size_t indexer_topk_ws(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dty
 struct ForwardWs {
   int64_t ld;
   bool fused;
-  size_t scores_off, indices_off, mla_off, total;
+  size_t scores_off, indices_off, topk_off, topk_bytes, mla_off, total;
 };
 
 ForwardWs forward_ws(const dsa_forward_args_t *a) {
@@ -185,6 +186,9 @@ ForwardWs forward_ws(const dsa_forward_args_t *a) {
     off += round_up(T * (size_t)w.ld * sizeof(float), 256);
   w.indices_off = off;
   if (!a->indices) off += round_up(T * (size_t)a->top_k * sizeof(int32_t), 256);
+  w.topk_off = off;
+  w.topk_bytes = w.fused ? 0 : dsa::topk_workspace_bytes(a->batch.num_queries, a->batch.max_k_len, a->top_k);
+  off += w.topk_bytes;
   w.mla_off = off;
   off += round_up(mla_ws(&a->batch, a->mla_dtype, a->heads, a->d_v, a->top_k), 256);
   w.total = off;
@@ -251,7 +255,7 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
   dsa_status_t st = check_batch(batch);
   if (st != DSA_OK) return st;
   if (k < 1 || k > 65536) return fail(DSA_ERR_INVALID_ARGUMENT, "top-k: k must be in [1, 65536] (got %d)", k);
-  *bytes = 0;
+  *bytes = dsa::topk_workspace_bytes(batch->num_queries, batch->max_k_len, k);
   return ok();
 }
 
@@ -296,8 +300,13 @@ dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_
   (void)workspace_bytes;
   dsa_status_t st = check_topk(batch, scores, ld_scores, k, indices);
   if (st != DSA_OK) return st;
+  const size_t need = dsa::topk_workspace_bytes(batch->num_queries, batch->max_k_len, k);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "top-k needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  if (need && !aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if (batch->num_queries == 0) return ok();
-  return hip_status(dsa::launch_topk(to_dev(batch), batch->num_queries, scores, ld_scores, k, indices, stream),
+  return hip_status(dsa::launch_topk(to_dev(batch), batch->num_queries, batch->max_k_len, scores, ld_scores, k,
+                                     indices, workspace, stream),
                     "top-k launch");
 }
 
@@ -378,7 +387,8 @@ dsa_status_t dsa_forward(const dsa_forward_args_t *a, void *workspace, size_t wo
     st = dsa_indexer_scores(&a->batch, &a->layout, a->index_dtype, a->h_i, a->d_i, a->q_idx, a->q_scale, a->w,
                             a->k_idx, a->k_scale, a->index_scale, scores, ws.ld, stream);
     if (st != DSA_OK) return st;
-    st = dsa_topk(&a->batch, scores, ws.ld, a->top_k, indices, nullptr, 0, stream);
+    st = dsa_topk(&a->batch, scores, ws.ld, a->top_k, indices, base ? base + ws.topk_off : nullptr, ws.topk_bytes,
+                  stream);
     if (st != DSA_OK) return st;
   }
   return dsa_sparse_mla_fwd(&a->batch, &a->layout, a->mla_dtype, a->heads, a->d_qk, a->d_v, a->q, a->kv, indices,
@@ -421,7 +431,9 @@ dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch, const dsa_kv_layout_t *k
   st = dsa_indexer_scores(batch, keys, dtype, h_i, d_i, q_idx, q_scale, w, k_idx, k_scale, scale, (float *)workspace,
                           ld, stream);
   if (st != DSA_OK) return st;
-  return dsa_topk(batch, (const float *)workspace, ld, k, indices, nullptr, 0, stream);
+  const size_t scores_bytes = round_up((size_t)batch->num_queries * ld * sizeof(float), 256);
+  return dsa_topk(batch, (const float *)workspace, ld, k, indices, (char *)workspace + scores_bytes,
+                  need - scores_bytes, stream);
 }
 
 dsa_status_t dsa_cache_append(const dsa_kv_layout_t *ly, int32_t num_tokens, const int32_t *seq, const int32_t *pos,

@@ -29,7 +29,7 @@ constexpr int kModuleMaxHidden = 16384;  // the scoring kernel stages u in LDS
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct ModuleWs {
-  size_t meta, q_idx, u, scores, q, q_abs, o_abs, y, mla, mla_bytes, total;
+  size_t meta, q_idx, u, scores, topk, topk_bytes, q, q_abs, o_abs, y, mla, mla_bytes, total;
   int64_t ld;
 };
 
@@ -42,6 +42,8 @@ ModuleWs module_ws(int32_t B, int32_t S, int32_t hidden, int32_t H, int32_t d_h,
   w.q_idx = take((size_t)B * d_i * 4);
   w.u = take((size_t)B * hidden * 4);
   w.scores = take((size_t)B * w.ld * 4);
+  w.topk_bytes = dsa::topk_workspace_bytes(B, S, S);  // the largest any top_k needs
+  w.topk = take(w.topk_bytes);
   w.q = take((size_t)B * H * d_h * 4);
   w.q_abs = take((size_t)B * H * d_c * 4);
   w.o_abs = take((size_t)B * H * d_c * 4);
@@ -124,7 +126,7 @@ dsa_status_t dsa_module_forward(int32_t batch, int32_t seq_len, int32_t hidden, 
       hipSuccess)
     return fail(e, "indexer scores");
   const dsa_batch_t bt{B, B, q_seq_start, k_len, 1, S};
-  dsa_status_t st = dsa_topk(&bt, scores, w.ld, top_k, indices, nullptr, 0, stream);
+  dsa_status_t st = dsa_topk(&bt, scores, w.ld, top_k, indices, base + w.topk, w.topk_bytes, stream);
   if (st != DSA_OK) return st;
   // softmax over the selected latent rows, per head, scale 1/sqrt(d_h)
   const dsa_kv_layout_t lat_ly{0, k_seq_start, nullptr, 0, 64, (int64_t)B * S};

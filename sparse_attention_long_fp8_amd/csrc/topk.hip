@@ -23,6 +23,8 @@
 //   4. one ordered pass writes key > tau, plus the first `need_eq` elements
 //      equal to tau, at positions given by block scans of per-thread (row in
 //      LDS) or per-wave (longer rows) counts: the output comes out ascending.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -119,24 +121,73 @@ __device__ __forceinline__ void load_chunk(const float *src, int base, int n, fl
   }
 }
 
+// Long rows in small batches are selected in two passes (launch_topk).  A
+// row's candidate list holds, part after part, the winners of each
+// kTkCache-long part of the row: min(k, part length) positions, ascending,
+// and their scores.  Part pass: workgroup (t, p) selects from its part and
+// writes its winners at the part's offset in the list.  Merge pass: the row's
+// list is the input row, and the positions its winners stand for are written.
+// Every element of the row's top-k has fewer than k elements ahead of it, in
+// its part too, so it is among its part's winners; list order is position
+// order, so ties still go to the lowest position.
+struct TopkSplit {
+  int32_t parts;    // 0: one pass
+  int32_t merge;    // 0: part pass, 1: merge pass
+  int32_t *cpos;    // [T, ld_c] candidate positions
+  float *cval;      // [T, ld_c] candidate scores
+  int64_t ld_c;     // list stride: >= the longest list, a multiple of 4
+};
+
+// Length of row t's candidate list up to (not including) part p.
+__device__ __forceinline__ int list_offset(int n_row, int k, int p) {
+  int off = 0;
+  for (int q = 0; q < p; ++q) off += min(k, min(max(n_row - q * kTkCache, 0), kTkCache));
+  return off;
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
                                                          const float *__restrict__ scores,
                                                          int64_t ld, int k,
-                                                         int32_t *__restrict__ indices) {
+                                                         int32_t *__restrict__ indices,
+                                                         TopkSplit sp) {
   __shared__ TopkLds sh;
   const int t = blockIdx.x;
   const int b = seq_of_row(bt, t);
-  const int n = candidates_of_row(bt, b, t);
+  const int n_row = candidates_of_row(bt, b, t);
+  int n = n_row;
+  const float *row = scores + (int64_t)t * ld;
   int32_t *out = indices + (int64_t)t * k;
+  int pos_off = 0;                   // part pass: first position of the part
+  const int32_t *pos_map = nullptr;  // merge pass: the positions list entries stand for
+  float *val_out = nullptr;          // part pass: scores of the winners
+  if (sp.parts > 0 && !sp.merge) {
+    const int p = blockIdx.y;
+    pos_off = p * kTkCache;
+    n = min(max(n_row - pos_off, 0), kTkCache);
+    row += pos_off;
+    const int64_t off = (int64_t)t * sp.ld_c + list_offset(n_row, k, p);
+    out = sp.cpos + off;
+    val_out = sp.cval + off;
+  } else if (sp.parts > 0) {
+    n = list_offset(n_row, k, sp.parts);
+    row = sp.cval + (int64_t)t * sp.ld_c;
+    pos_map = sp.cpos + (int64_t)t * sp.ld_c;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
   if (n <= k) {  // every candidate is kept
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    if (val_out) {  // part pass: the whole part, no padding (the next part's entries follow)
+      for (int i = tid; i < n; i += kTkThreads) {
+        out[i] = pos_off + i;
+        val_out[i] = row[i];
+      }
+    } else {
+      for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? (pos_map ? pos_map[i] : i) : -1;
+    }
     return;
   }
-  const float *row = scores + (int64_t)t * ld;
   // The first sweep keeps the row's first chunk (all of it when n <= 32768)
   // in LDS; every later sweep reads that chunk from there.
   static_assert(kChunk == kTkCache, "the cached part of a row is its first sweep chunk");
@@ -348,6 +399,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   const int need_eq = need;
 
   // ---- 4. ordered write: key > tau, then the first need_eq keys == tau ----
+  // (a part pass always holds its part in LDS: parts are kTkCache long)
+  auto emit = [&](int pos, int pos_i) __attribute__((always_inline)) {
+    out[pos] = pos_map ? pos_map[pos_i] : pos_off + pos_i;
+    if (val_out) val_out[pos] = sh.cache[pos_i];
+  };
   int gt_run = 0, eq_run = 0;
   if (cached) {
     // The row is in LDS, one piece of runs (above).  Each thread holds
@@ -410,12 +466,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
         const int pos_i = r0 + bit;
         if ((gtm >> bit) & 1u) {
           const int pos = g_before + min(e_before, need_eq);
-          if (pos < k) out[pos] = pos_i;
+          if (pos < k) emit(pos, pos_i);
           ++g_before;
         } else {
           if (e_before < need_eq) {
             const int pos = g_before + e_before;
-            if (pos < k) out[pos] = pos_i;
+            if (pos < k) emit(pos, pos_i);
           }
           ++e_before;
         }
@@ -499,12 +555,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
           const int pos_i = s0 + 256 * u + j;
           if ((gn >> j) & 1u) {
             const int pos = gpos + min(epos, need_eq);
-            if (pos < k) out[pos] = pos_i;
+            if (pos < k) emit(pos, pos_i);
             ++gpos;
           } else {
             if (epos < need_eq) {
               const int pos = gpos + epos;
-              if (pos < k) out[pos] = pos_i;
+              if (pos < k) emit(pos, pos_i);
             }
             ++epos;
           }
@@ -517,15 +573,50 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     }
   }
   const int total = gt_run + min(eq_run, need_eq);
-  for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
+  if (!val_out)
+    for (int i = total + tid; i < k; i += kTkThreads) out[i] = -1;
 #undef DSA_SWEEP_CHUNK
 }
 
-hipError_t launch_topk(const BatchDev &bt, int num_queries, const float *scores, int64_t ld,
-                       int k, int32_t *indices, hipStream_t stream) {
+// Few rows with histories past the LDS row cache leave most CUs idle while
+// one workgroup sweeps each long row; such batches take the two passes.
+static int topk_parts(int num_queries, int max_k_len) {
+  if (num_queries >= 256 || max_k_len <= kTkCache) return 0;
+  return (max_k_len + kTkCache - 1) / kTkCache;
+}
+
+// List stride: a row's list holds min(k, part length) per part, never more
+// than the row itself.
+static int64_t topk_list_ld(int parts, int k, int max_k_len) {
+  return (std::min((int64_t)parts * k, (int64_t)max_k_len) + 3) / 4 * 4;
+}
+
+size_t topk_workspace_bytes(int num_queries, int max_k_len, int k) {
+  const int parts = topk_parts(num_queries, max_k_len);
+  if (!parts) return 0;
+  const size_t list = (size_t)num_queries * topk_list_ld(parts, k, max_k_len) * 4;
+  return (list + 255) / 256 * 256 * 2;  // positions, then scores
+}
+
+hipError_t launch_topk(const BatchDev &bt, int num_queries, int max_k_len, const float *scores, int64_t ld,
+                       int k, int32_t *indices, void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld,
-                     k, indices);
+  TopkSplit sp{};
+  sp.parts = topk_parts(num_queries, max_k_len);
+  if (!sp.parts) {
+    hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k, indices,
+                       sp);
+    return hipGetLastError();
+  }
+  sp.ld_c = topk_list_ld(sp.parts, k, max_k_len);
+  const size_t list = ((size_t)num_queries * sp.ld_c * 4 + 255) / 256 * 256;
+  sp.cpos = (int32_t *)workspace;
+  sp.cval = (float *)((char *)workspace + list);
+  hipLaunchKernelGGL(topk_kernel, dim3(num_queries, sp.parts), dim3(kTkThreads), 0, stream, bt, scores, ld, k,
+                     indices, sp);
+  sp.merge = 1;
+  hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k, indices,
+                     sp);
   return hipGetLastError();
 }
 

@@ -90,6 +90,10 @@ class DeviceWorkload:
         self.ws_bytes = B.dsa_sparse_mla_workspace_size(self.batch, self.mla_dtype, wl.heads, wl.d_qk, wl.d_v,
                                                         wl.top_k)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        # top-k of few long rows runs in two passes over a candidate-list workspace (256-byte aligned)
+        self.topk_ws_bytes = B.dsa_topk_workspace_size(self.batch, wl.top_k)
+        self.topk_ws = torch.empty(self.topk_ws_bytes + 256, dtype=torch.uint8, device=dev)
+        self.topk_ws_ptr = self.topk_ws.data_ptr() + (-self.topk_ws.data_ptr()) % 256
 
     # ---- the three stages (exactly what dsa_forward enqueues) ----
     def indexer(self, copy=0, stream=None):
@@ -99,7 +103,8 @@ class DeviceWorkload:
                              wl.index_scale, self.scores, self.ld, stream=stream)
 
     def topk(self, stream=None):
-        B.dsa_topk(self.batch, self.scores, self.ld, self.wl.top_k, self.idx, stream=stream)
+        B.dsa_topk(self.batch, self.scores, self.ld, self.wl.top_k, self.idx, self.topk_ws_ptr, self.topk_ws_bytes,
+                   stream=stream)
 
     def mla(self, copy=0, stream=None):
         wl = self.wl

@@ -108,7 +108,10 @@ class GpuCase:
     def topk(self, scores, ld=None, k=None):
         k = k or self.wl.top_k
         idx = torch.full((self.T, k), -7, dtype=torch.int32, device=self.dev)
-        B.dsa_topk(self.batch, scores, ld or scores.shape[1], k, idx)
+        nb = B.dsa_topk_workspace_size(self.batch, k)
+        ws = torch.empty(nb + 256, dtype=torch.uint8, device=self.dev) if nb else None
+        base = ws.data_ptr() + (-ws.data_ptr()) % 256 if nb else None
+        B.dsa_topk(self.batch, scores, ld or scores.shape[1], k, idx, base, nb)
         return idx
 
     def mla(self, idx, k=None):

@@ -2,8 +2,9 @@
 heavy ties (small bins resolved by ranking, large ones by radix digits), a
 constant row (the whole row is one bin, past the candidate list), signed
 zeros, all-negative rows, rows longer than the LDS row cache, rows
-shorter than k, ReLU rows that are half exact zeros, and k above the 2048
-outputs assembled in LDS.  Each row is its own sequence, so n_t = k_len[t]; entries
+shorter than k, ReLU rows that are half exact zeros, k above 2048, and
+ties spread over the parts of rows longer than 32768 (selected in two passes
+when the batch has few rows).  Each row is its own sequence, so n_t = k_len[t]; entries
 past n_t are NaN and must never be read."""
 
 import zlib
@@ -36,13 +37,16 @@ def _rows(kind, rng):
         return [np.maximum(rng.standard_normal(16384), 0).astype(np.float32) for _ in range(2)], 512
     if kind == "k_above_staging":   # more outputs than the LDS staging holds: direct stores
         return [rng.standard_normal(20000).astype(np.float32), rng.integers(0, 50, 40000).astype(np.float32)], 3000
+    if kind == "long_ties":   # ties across the 32768-long parts of a two-pass selection
+        return [np.full(70000, 2.5, np.float32), rng.integers(0, 4, 90000).astype(np.float32)], 5000
     if kind == "short_rows":
         return [rng.standard_normal(n).astype(np.float32) for n in (1, 10, 63, 64, 65)], 64
     raise KeyError(kind)
 
 
 @pytest.mark.parametrize("kind", ["ties_small_bins", "ties_few_values", "constant", "signed_zero",
-                                  "all_negative", "long_rows", "short_rows", "relu_zeros", "k_above_staging"])
+                                  "all_negative", "long_rows", "short_rows", "relu_zeros", "k_above_staging",
+                                  "long_ties"])
 def test_topk_crafted_rows(kind, gpu):
     print("\n[topk-edge] %s" % kind, flush=True)
     rng = np.random.default_rng(zlib.crc32(kind.encode()))
@@ -58,7 +62,10 @@ def test_topk_crafted_rows(kind, gpu):
     batch = B.make_batch(q_seq_start, k_len, T, T, 1, max(ns))
     d_scores = torch.from_numpy(scores).to(gpu)
     idx = torch.full((T, k), -7, dtype=torch.int32, device=gpu)
-    B.dsa_topk(batch, d_scores, ld, k, idx)
+    nb = B.dsa_topk_workspace_size(batch, k)   # rows past 32768 in a small batch: two passes
+    ws = torch.empty(nb + 256, dtype=torch.uint8, device=gpu) if nb else None
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256 if nb else None
+    B.dsa_topk(batch, d_scores, ld, k, idx, base, nb)
     torch.cuda.synchronize()
     got = idx.cpu().numpy().astype(np.int64)
     for t, r in enumerate(rows):
