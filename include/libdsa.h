@@ -158,7 +158,8 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
  * cache, for batches with max_q_per_seq >= 8 (prefill, chunked prefill);
  * its workspace holds (2k + 128, rounded up to 64) candidates of 8 bytes per
  * query row.  Other shapes run the two stages with the fp32 score rows in
- * the workspace.  Arguments as for the two stages; workspace 256-byte
+ * the workspace, followed by dsa_topk's own workspace when it needs one.
+ * Arguments as for the two stages; workspace 256-byte
  * aligned, dsa_indexer_topk_workspace_size() bytes.
  * ---------------------------------------------------------------------- */
 dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch, const dsa_kv_layout_t *keys,
