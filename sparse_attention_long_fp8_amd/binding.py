@@ -142,18 +142,28 @@ def _check(status, where):
         raise DsaError(status, where, dsa_last_error())
 
 
+# The descriptors hold raw device pointers; each keeps a reference to the
+# tensors it points at (`_keep`), so that a temporary passed in is not freed
+# (and its memory handed to another tensor) while the descriptor is in use.
+
 def make_batch(q_seq_start, k_len, num_seqs, num_queries, max_q_per_seq, max_k_len):
     """dsa_batch_t from device int32 tensors and host-side counts / bounds."""
-    return dsa_batch_t(int(num_seqs), int(num_queries), _p(q_seq_start), _p(k_len), int(max_q_per_seq),
-                       int(max_k_len))
+    bt = dsa_batch_t(int(num_seqs), int(num_queries), _p(q_seq_start), _p(k_len), int(max_q_per_seq),
+                     int(max_k_len))
+    bt._keep = (q_seq_start, k_len)
+    return bt
 
 
 def make_contiguous_layout(k_seq_start, num_rows):
-    return dsa_kv_layout_t(0, _p(k_seq_start), None, 0, 64, int(num_rows))
+    ly = dsa_kv_layout_t(0, _p(k_seq_start), None, 0, 64, int(num_rows))
+    ly._keep = (k_seq_start,)
+    return ly
 
 
 def make_paged_layout(page_table, stride, num_pages, page_size=64):
-    return dsa_kv_layout_t(1, None, _p(page_table), int(stride), int(page_size), int(num_pages))
+    ly = dsa_kv_layout_t(1, None, _p(page_table), int(stride), int(page_size), int(num_pages))
+    ly._keep = (page_table,)
+    return ly
 
 
 # --------------------------------------------------------------------------

@@ -401,16 +401,31 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;    // lane group
   const int n16 = lane & 15;  // column within a 16-wide tile
-  const int b = seq_of_row(bt, t);
   const int slot_begin = split * slots_per_split;
   const int slot_end = min(k, slot_begin + slots_per_split);
   const int nslot = max(slot_end - slot_begin, 0);
   const int nblk = (nslot + kBlk - 1) / kBlk;
   const int32_t *idx_t = idx + (int64_t)t * k;
   const uint8_t *kv_bytes = (const uint8_t *)kv;
-  const int64_t row0 = key_row(kd, b, 0);  // stand-in row for masked / pad slots
 
-  // query operand (B of S^T): heads HW*w + 16*ht + n16, dims 32*ks + 8g .. +8
+  // Prologue order: loads whose results are needed first go out first, so
+  // that waiting for them leaves the (large) query loads in flight.
+  // (1) this thread's selected positions
+  constexpr int kPer = kMaxSlots / NT;
+  static_assert(kPer * NT == kMaxSlots, "slots split evenly over the threads");
+  int sel[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * NT;
+    sel[u] = i < nslot ? idx_t[slot_begin + i] : -1;
+  }
+  // (2) first round of a 64-ary search for the row's sequence: lane l reads
+  // q_seq_start[l * step]
+  const int step0 = (bt.num_seqs + 63) >> 6;
+  const int pos0 = lane * step0;
+  const int qs0 = pos0 < bt.num_seqs ? bt.q_seq_start[pos0] : 0x7FFFFFFF;
+  __builtin_amdgcn_sched_barrier(0);
+  // (3) query operand (B of S^T): heads HW*w + 16*ht + n16, dims 32*ks + 8g .. +8
   v8bf qf[HT][kKs];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -418,12 +433,29 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) qf[ht][ks] = *(const v8bf *)(qh + 32 * ks);
   }
-  // resolve every slot of the range once
-  for (int i = tid; i < nblk * kBlk; i += NT) {
-    const int s = i < nslot ? idx_t[slot_begin + i] : -1;
-    sh.rows[i] = s >= 0 ? (int32_t)key_row(kd, b, s) : -1;
+  __builtin_amdgcn_sched_barrier(0);
+  // the sequence: the last entry of q_seq_start that is <= t (entries are
+  // non-decreasing; the lanes reading such entries form a prefix).  Later
+  // rounds only run for more than 64 sequences.  Kept in [0, num_seqs) for
+  // any array contents.
+  int b = max((int)__popcll(__ballot(qs0 <= t)) - 1, 0) * step0;
+  for (int span = min(step0, bt.num_seqs - b); span > 1;) {
+    const int step = (span + 63) >> 6;
+    const int pos = b + lane * step;
+    const bool le = pos < b + span && bt.q_seq_start[pos] <= t;
+    const int c = max((int)__popcll(__ballot(le)), 1);
+    b += (c - 1) * step;
+    span = min(step, span - (c - 1) * step);
   }
-  __syncthreads();
+  b = __builtin_amdgcn_readfirstlane(b);
+  const int64_t row0 = key_row(kd, b, 0);  // stand-in row for masked / pad slots
+  // (4) resolve every slot of the range once
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * NT;
+    if (i < nblk * kBlk) sh.rows[i] = sel[u] >= 0 ? (int32_t)key_row(kd, b, sel[u]) : -1;
+  }
+  lds_barrier();  // LDS only: the query loads stay in flight
 
   // tile blk -> buffer buf: wave-wide load j of wave w fills LDS slots
   // 64*(NW*j + w) .. +63; slot -> (row = slot / 74, chunk = slot % 74); chunks
@@ -470,10 +502,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
 
   // The query loads must be complete (and known complete to the compiler)
   // before the tile loop: otherwise its wait bookkeeping re-waits for them in
-  // every iteration, draining the tile loads kept in flight.
+  // every iteration, draining the tile loads kept in flight.  They complete
+  // together with tile 0's gather; the next tiles go out after.
+  if (nblk > 0) gather(0, 0);
   wait_vmcnt<0>();
-  for (int p = 0; p < kBufs - 1 && p < nblk; ++p) gather(p, p);
-  wait_tiles(min(nblk, kBufs - 1) - 1);  // tile 0 landed
+  for (int p = 1; p < kBufs - 1 && p < nblk; ++p) gather(p, p);
   lds_barrier();
 
   for (int blk = 0; blk < nblk; ++blk) {

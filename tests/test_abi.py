@@ -87,6 +87,15 @@ def test_workspace_sizes_and_too_small():
     pre = B.dsa_batch_t(1, 16384, 0x1000, 0x2000, 16384, 16384)
     assert B.dsa_sparse_mla_workspace_size(pre, B.DSA_BF16, 128, 576, 512, 2048) == 0
     assert B.dsa_topk_workspace_size(pre, 2048) == 0
+    # top-k in two passes (32768-long parts): candidate positions and scores,
+    # [T, round4(min(parts * k, max_k_len))] each, 256-byte aligned
+    def tk(T, max_k_len, k):
+        return B.dsa_topk_workspace_size(B.dsa_batch_t(T, T, 0x1000, 0x2000, 1, max_k_len), k)
+    assert tk(32, 32768, 2048) == 0                          # rows fit the LDS cache: one pass
+    assert tk(32, 32769, 2048) == 2 * 32 * 4096 * 4          # a one-score second part
+    assert tk(255, 70000, 2048) == 2 * 255 * 6144 * 4        # three parts
+    assert tk(255, 70000, 30000) == 2 * (-(-255 * 70000 * 4 // 256) * 256)  # the list never exceeds the row
+    assert tk(256, 70000, 2048) == 0                         # enough rows to fill the chip
     st = B.dsa_sparse_mla_fwd(dec, _layout(1 << 20), B.DSA_BF16, 128, 576, 512, 0x100, 0x200, 0x300, 2048, 0.04,
                               0x400, None, None, ws - 1, check=False)
     assert st == B.DSA_ERR_WORKSPACE_TOO_SMALL
@@ -198,3 +207,22 @@ def test_validate_argument_errors():
     assert B.dsa_validate(bt, paged, None, 0, None, 0, 0x100, check=False) == B.DSA_ERR_UNSUPPORTED   # page size
     bad = B.dsa_batch_t(0, 4, 0x1000, 0x2000, 4, 8)
     assert B.dsa_validate(bad, ly, None, 0, None, 0, 0x100, check=False) == B.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_descriptors_keep_their_arrays_alive():
+    # the descriptors carry raw pointers: a temporary array passed in must live
+    # as long as the descriptor, or its memory could be handed to another tensor
+    import gc
+    import weakref
+    import torch
+    arrs = [torch.arange(5, dtype=torch.int32), torch.ones(4, dtype=torch.int32), torch.zeros(2, dtype=torch.int64),
+            torch.zeros((4, 3), dtype=torch.int32)]
+    refs = [weakref.ref(a) for a in arrs]
+    held = [B.make_batch(arrs[0], arrs[1], 4, 4, 1, 10), B.make_contiguous_layout(arrs[2], 10),
+            B.make_paged_layout(arrs[3], 3, 12)]
+    del arrs
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del held
+    gc.collect()
+    assert all(r() is None for r in refs)

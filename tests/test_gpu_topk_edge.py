@@ -2,9 +2,11 @@
 heavy ties (small bins resolved by ranking, large ones by radix digits), a
 constant row (the whole row is one bin, past the candidate list), signed
 zeros, all-negative rows, rows longer than the LDS row cache, rows
-shorter than k, ReLU rows that are half exact zeros, k above 2048, and
-ties spread over the parts of rows longer than 32768 (selected in two passes
-when the batch has few rows).  Each row is its own sequence, so n_t = k_len[t]; entries
+shorter than k, ReLU rows that are half exact zeros, k above 2048, ties
+spread over the parts of rows longer than 32768 (selected in two passes when
+the batch has few rows), and crafted rows of 16385 to 32768 scores in a
+small batch with k = 4096 and 4097 (ties across position 16384, ragged
+lengths).  Each row is its own sequence, so n_t = k_len[t]; entries
 past n_t are NaN and must never be read."""
 
 import zlib
@@ -39,6 +41,12 @@ def _rows(kind, rng):
         return [rng.standard_normal(20000).astype(np.float32), rng.integers(0, 50, 40000).astype(np.float32)], 3000
     if kind == "long_ties":   # ties across the 32768-long parts of a two-pass selection
         return [np.full(70000, 2.5, np.float32), rng.integers(0, 4, 90000).astype(np.float32)], 5000
+    if kind == "mid_ties":     # ties across position 16384, ragged rows
+        return [np.full(30000, 0.5, np.float32), rng.integers(0, 4, 25000).astype(np.float32),
+                rng.standard_normal(1000).astype(np.float32), rng.integers(0, 2, 16385).astype(np.float32),
+                np.concatenate([np.zeros(16384, np.float32), np.ones(8000, np.float32)])], 4096
+    if kind == "mid_k_limit":
+        return [np.full(30000, 0.5, np.float32), rng.integers(0, 4, 25000).astype(np.float32)], 4097
     if kind == "short_rows":
         return [rng.standard_normal(n).astype(np.float32) for n in (1, 10, 63, 64, 65)], 64
     raise KeyError(kind)
@@ -46,7 +54,7 @@ def _rows(kind, rng):
 
 @pytest.mark.parametrize("kind", ["ties_small_bins", "ties_few_values", "constant", "signed_zero",
                                   "all_negative", "long_rows", "short_rows", "relu_zeros", "k_above_staging",
-                                  "long_ties"])
+                                  "long_ties", "mid_ties", "mid_k_limit"])
 def test_topk_crafted_rows(kind, gpu):
     print("\n[topk-edge] %s" % kind, flush=True)
     rng = np.random.default_rng(zlib.crc32(kind.encode()))
