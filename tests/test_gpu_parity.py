@@ -31,6 +31,13 @@ SMALL = {
     # the other MLA head counts: 64 (one workgroup per row and range) and 32
     "decode_h64": W("decode_h64", 17, "decode", 3, 0, ctx_range=(300, 1500), top_k=192, heads=64),
     "prefill_h32mla": W("prefill_h32mla", 18, "prefill", 1, 160, top_k=100, heads=32),
+    # the other FP8 indexer head counts on the staged kernel: 128 heads (decode, and a chunk of 24 queries per
+    # sequence, which the tiled kernel does not take at 128 heads) and 32 heads over paged keys
+    "decode_hi128": W("decode_hi128", 24, "decode", 3, 0, ctx_range=(300, 2500), h_i=128, top_k=128),
+    "chunk_hi128": W("chunk_hi128", 25, "chunk", 2, 0, ctx_range=(300, 900), q_per_seq=24, h_i=128, top_k=64,
+                     heads=16),
+    "decode_hi32_paged": W("decode_hi32_paged", 26, "decode", 3, 0, ctx_range=(70, 1500), paged=True, h_i=32,
+                           top_k=64),
 }
 
 
