@@ -38,6 +38,8 @@ SMALL = {
                      heads=16),
     "decode_hi32_paged": W("decode_hi32_paged", 26, "decode", 3, 0, ctx_range=(70, 1500), paged=True, h_i=32,
                            top_k=64),
+    # chunked prefill over paged keys (the tiled indexer kernel resolving page bases; poisoned page tails)
+    "chunk_paged": W("chunk_paged", 27, "chunk", 2, 0, ctx_range=(300, 900), q_per_seq=40, paged=True, top_k=96),
 }
 
 
