@@ -98,7 +98,14 @@ def kernel_name(stage, wl, lay):
         return "indexer_fp8_tiled_kernel" if lay.max_q_per_seq >= 8 and wl.h_i == 64 else "indexer_fp8_staged_kernel"
     if stage == "topk":
         return "topk_kernel"
-    return "mla_bf16_kernel" if wl.fp8 else "mla_f32_kernel"
+    if not wl.fp8:
+        return "mla_f32_kernel"
+    # the bf16 launcher's split count: about one workgroup per CU, at least four
+    # 32-slot tiles and at most 2048 slots per range, at most 32 ranges
+    T, k = lay.num_queries, wl.top_k
+    s = min(-(-256 // max(T, 1)), -(-k // 128))
+    s = min(max(s, -(-k // 2048)), 32)
+    return "mla_bf16_kernel + mla_combine_kernel" if s > 1 else "mla_bf16_kernel"
 
 
 def source_hash(stage):
