@@ -197,7 +197,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   else load_chunk(row, base, n, v);
 
   // ---- 1. cache the row, min / max key ----
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // (min / max on the values; the keys of the two extremes are taken once,
+  // which folds -0 onto +0 as the keys of every element would)
+  float vmin = INFINITY, vmax = -INFINITY;
   for (int base = 0; base < n; base += kChunk) {
     float4 v[kU];
     load_chunk(row, base, n, v);
@@ -205,18 +207,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     for (int u = 0; u < kU; ++u) {
       const int i = base + 4 * (tid + u * kTkThreads);
       if (base == 0 && i < n) *(float4 *)(&sh.cache[i]) = v[u];
-      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      if (i + 3 < n) {
+        vmin = fminf(vmin, fminf(fminf(v[u].x, v[u].y), fminf(v[u].z, v[u].w)));
+        vmax = fmaxf(vmax, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+      } else {
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i + j < n) {
-          const uint32_t key = float_key(f[j]);
-          kmin = min(kmin, key);
-          kmax = max(kmax, key);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (i + j < n) {
+            vmin = fminf(vmin, f[j]);
+            vmax = fmaxf(vmax, f[j]);
+          }
+      }
     }
   }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
+  uint32_t kmin = wave_min_u32(float_key(vmin));
+  uint32_t kmax = wave_max_u32(float_key(vmax));
   if (lane == 0) { sh.red_lo[wave] = kmin; sh.red_hi[wave] = kmax; }
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   lds_barrier();
@@ -230,8 +236,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   const float fmax = key_to_float(kmax);
   float inv = (float)kTkBins / (fmax - fmin);
   if (!(fmax > fmin) || !(inv < 3.0e38f)) inv = 0.f;  // degenerate range: one bin
+  // (a NaN score, a precondition violation, converts to bin 0)
   auto bin_of = [&](float f) -> int {
-    return (int)fminf(fmaxf((f - fmin) * inv, 0.f), (float)(kTkBins - 1));
+    return (int)__builtin_amdgcn_fmed3f((f - fmin) * inv, 0.f, (float)(kTkBins - 1));
   };
 
   // ---- 2. histogram, threshold bin ----
@@ -246,9 +253,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
     for (int u = 0; u < kU; ++u) {
       const int i = base + 4 * (tid + u * kTkThreads);
       const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const bool whole = i + 3 < n;  // no per-element bound test inside the row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (i + j < n) {
+        if (whole || i + j < n) {
           const int bn = bin_of(f[j]);
           if (bn == 0)
             ++low;
@@ -295,9 +303,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
       if (i >= n) continue;
       const float4 v = *(const float4 *)(&sh.cache[i]);
       const float f[4] = {v.x, v.y, v.z, v.w};
+      const bool whole = i + 3 < n;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (i + j >= n) break;
+        if (!whole && i + j >= n) break;
         const int bn = bin_of(f[j]);
         above_bin |= (uint32_t)(bn > bstar) << (4 * qq + j);
         if (bn == bstar) {
