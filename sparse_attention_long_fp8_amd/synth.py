@@ -333,16 +333,22 @@ class Synth:
         """Physical pools for the paged layout, with unused slots poisoned.
 
         Returns (ki_pool [P,64,d_I] uint8, ki_scale_pool [P,64] f32,
-        kv_pool [P,64,D_qk] uint16).  Slots past a history's end hold NaN
-        patterns (E4M3 0x7F, scale NaN, bfloat16 0x7FC0) so that any read of
+        kv_pool [P,64,D_qk] uint16), or for fp32 workloads (ki_pool f32,
+        None, kv_pool f32).  Slots past a history's end hold NaN patterns
+        (E4M3 0x7F, scale NaN, bfloat16 0x7FC0, fp32 NaN) so that any read of
         them shows up in the results.
         """
         wl, lay = self.wl, self.layout
-        assert wl.paged and wl.fp8
+        assert wl.paged
         P = lay.num_pages
-        ki_pool = np.full((P, PAGE_SIZE, wl.d_i), 0x7F, dtype=np.uint8)
-        ks_pool = np.full((P, PAGE_SIZE), np.nan, dtype=np.float32)
-        kv_pool = np.full((P, PAGE_SIZE, wl.d_qk), 0x7FC0, dtype=np.uint16)
+        if wl.fp8:
+            ki_pool = np.full((P, PAGE_SIZE, wl.d_i), 0x7F, dtype=np.uint8)
+            ks_pool = np.full((P, PAGE_SIZE), np.nan, dtype=np.float32)
+            kv_pool = np.full((P, PAGE_SIZE, wl.d_qk), 0x7FC0, dtype=np.uint16)
+        else:
+            ki_pool = np.full((P, PAGE_SIZE, wl.d_i), np.nan, dtype=np.float32)
+            ks_pool = None
+            kv_pool = np.full((P, PAGE_SIZE, wl.d_qk), np.nan, dtype=np.float32)
         for b in range(wl.batch):
             n = int(lay.k_len[b])
             base = int(lay.k_seq_start[b])
@@ -355,6 +361,7 @@ class Synth:
                 pages = lay.page_table[b, s // PAGE_SIZE]
                 slots = s % PAGE_SIZE
                 ki_pool[pages, slots] = codes
-                ks_pool[pages, slots] = sc
+                if ks_pool is not None:
+                    ks_pool[pages, slots] = sc
                 kv_pool[pages, slots] = kvb
         return ki_pool, ks_pool, kv_pool

@@ -86,8 +86,8 @@ class GpuCase:
         if self.paged:
             ki_pool, ks_pool, kv_pool = s.paged_pools()
             self.ki = torch.from_numpy(ki_pool).to(dev)
-            self.ks = torch.from_numpy(ks_pool).to(dev)
-            self.kv = _bf16(kv_pool, dev)
+            self.ks = torch.from_numpy(ks_pool).to(dev) if ks_pool is not None else None
+            self.kv = _bf16(kv_pool, dev) if wl.fp8 else torch.from_numpy(kv_pool).to(dev)
             self.page_table = _i32(lay.page_table, dev)
             self.layout = B.make_paged_layout(self.page_table, lay.page_table.shape[1], lay.num_pages)
         else:

@@ -40,6 +40,12 @@ SMALL = {
                            top_k=64),
     # chunked prefill over paged keys (the tiled indexer kernel resolving page bases; poisoned page tails)
     "chunk_paged": W("chunk_paged", 27, "chunk", 2, 0, ctx_range=(300, 900), q_per_seq=40, paged=True, top_k=96),
+    # fp32 path away from the tiny shape: odd sizes (7 x 100 indexer, 5 heads, 53-wide keys, 40-wide values:
+    # scalar gathers) in chunks, and the largest fp32 shape (64 x 128 indexer, 64 heads, 256 / 192) over pages
+    "f32_chunk_odd": W("f32_chunk_odd", 28, "chunk", 3, 0, ctx_range=(60, 500), q_per_seq=6, h_i=7, d_i=100,
+                       fp8=False, top_k=48, heads=5, d_c=40, d_r=13),
+    "f32_paged_max": W("f32_paged_max", 29, "decode", 4, 0, ctx_range=(70, 900), paged=True, h_i=64, d_i=128,
+                       fp8=False, top_k=100, heads=64, d_c=192, d_r=64),
 }
 
 

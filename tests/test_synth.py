@@ -118,3 +118,24 @@ def test_paged_pools_poison_and_map():
         if tail:
             assert (ki_pool[last, tail:] == 0x7F).all() and np.isnan(ks_pool[last, tail:]).all()
             assert (kv_pool[last, tail:] == 0x7FC0).all()
+
+
+def test_paged_pools_fp32():
+    # fp32 workloads: fp32 key and latent pools, no scales, NaN in unused slots
+    wl = synth.Workload("paged_small_f32", 5, "decode", 3, 0, ctx_range=(70, 200), paged=True,
+                        h_i=2, d_i=16, fp8=False, top_k=8, heads=2, d_c=8, d_r=8)
+    s = synth.Synth(wl)
+    lay = s.layout
+    ki_pool, ks_pool, kv_pool = s.paged_pools()
+    assert ks_pool is None and ki_pool.dtype == np.float32 and kv_pool.dtype == np.float32
+    for b in range(wl.batch):
+        n = int(lay.k_len[b])
+        base = int(lay.k_seq_start[b])
+        k, none = s.ki(base, base + n)
+        assert none is None
+        assert np.array_equal(O.unpage(ki_pool, lay.page_table[b], n, 64), k)
+        assert np.array_equal(O.unpage(kv_pool, lay.page_table[b], n, 64), s.kv(base, base + n))
+        last = lay.page_table[b, (n - 1) // 64]
+        tail = n % 64
+        if tail:
+            assert np.isnan(ki_pool[last, tail:]).all() and np.isnan(kv_pool[last, tail:]).all()
