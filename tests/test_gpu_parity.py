@@ -46,6 +46,10 @@ SMALL = {
                        fp8=False, top_k=48, heads=5, d_c=40, d_r=13),
     "f32_paged_max": W("f32_paged_max", 29, "decode", 4, 0, ctx_range=(70, 900), paged=True, h_i=64, d_i=128,
                        fp8=False, top_k=100, heads=64, d_c=192, d_r=64),
+    # selections longer than the 2048 slots one attention workgroup resolves: two ranges and a merge even in
+    # prefill (and the fused indexer -> top-k at k = 2200), and 32 ranges a row for two decodes at k = 4096
+    "prefill_k2200": W("prefill_k2200", 30, "prefill", 1, 2600, top_k=2200, heads=16),
+    "decode_k4096": W("decode_k4096", 33, "decode", 2, 0, ctx_range=(5000, 9000), top_k=4096),
 }
 
 
