@@ -2,16 +2,18 @@
 """Throughput of the DSA hot path (lightning indexer -> top-k -> sparse MLA)
 on one MI355X, through the libdsa C ABI.
 
-A step is one pass of the whole path over the workload's batch: the three
-stages are launched back to back on torch's current stream (exactly what
-dsa_forward enqueues), with HIP events between them so that every stage's
-average duration is measured live over the timed region.  Inputs are
-resident in HBM before timing starts; for the decode workloads several
-copies of every input are rotated so that no step finds its inputs in the
-256 MB Infinity Cache left there by the previous one.
+A step is one dsa_forward call over the workload's batch (indexer, top-k and
+sparse MLA, with the split merge where the selections are split).  Inputs are
+resident in HBM before timing starts; for the decode workloads several copies
+of every input are rotated so that no step finds its inputs in the 256 MB
+Infinity Cache left there by the previous one.  A second loop runs the same
+passes stage by stage with HIP events recorded around each stage on the
+launch stream, which gives every stage's average duration for the rooflines.
 
-Prints one JSON line.  Default workload: 32 single-token decodes over 32768
-cached tokens (FP8 indexer 64x128, k = 2048, 128-head 576/512 bf16 MLA).
+Prints one JSON line.  The headline workload (default) is the causal prefill
+of 65536 tokens: FP8 indexer 64 x 128, k = 2048, 128-head 576/512 bf16 MLA,
+keys with a per-256-token block drift.  The same line carries a `workloads`
+object with the other four workloads, each built, timed and freed in turn.
 """
 
 from __future__ import annotations
@@ -33,17 +35,27 @@ HBM_PEAK = 8.0e12      # bytes/s, MI355X HBM3E
 FP8_PEAK = 5.0e15      # dense FP8 MFMA flop/s
 BF16_PEAK = 2.5e15     # dense BF16 MFMA flop/s
 PROFILES = os.path.join(ROOT, "profiles")
+# the headline: the largest workload that fits one GPU, the long causal prefill
+HEADLINE = "prefill_64k"
+ALL_WORKLOADS = ("prefill_64k", "prefill_16k", "decode_32k", "paged_decode", "tiny_prefill")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 200 decode, 10 prefill)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: 20 decode, 3 prefill)")
-    ap.add_argument("--workload", default="decode_32k",
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps of the headline workload (default: 10 prefill, 200 decode)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: 3 prefill, 20 decode)")
+    ap.add_argument("--workload", default=HEADLINE,
                     help="decode_32k | prefill_16k | prefill_64k | paged_decode | tiny_prefill")
+    ap.add_argument("--others", default="all",
+                    help="the other workloads measured into the line's `workloads` object: "
+                         "all (default), none, or a comma-separated list")
     ap.add_argument("--copies", type=int, default=None, help="input copies rotated across steps")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work for the baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for the baseline (decode and small prefill workloads)")
+    ap.add_argument("--cpu-sample", type=int, default=256,
+                    help="query rows of the oracle sample on prefill workloads past 16384 rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel on MIB mebibytes (counter calibration) and exit")
@@ -108,6 +120,13 @@ def kernel_name(stage, wl, lay):
     return "mla_bf16_kernel + mla_combine_kernel" if s > 1 else "mla_bf16_kernel"
 
 
+def fused_applies(wl, lay):
+    """Whether dsa_forward without kept scores takes the fused indexer ->
+    top-k kernel (the launcher's choice): FP8, 64 x 128 indexer heads,
+    contiguous keys, at least 8 query rows per sequence."""
+    return wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and not wl.paged and lay.max_q_per_seq >= 8
+
+
 def source_hash(stage):
     path = os.path.join(ROOT, "sparse_attention_long_fp8_amd", "csrc", KERNEL_SOURCES[stage])
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -128,16 +147,102 @@ def traffic_of(stage, workload):
 # --------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # --------------------------------------------------------------------------
-def cpu_baseline(wl, synth_obj, budget_s):
+def host_info():
+    """BLAS threads the oracle runs on, the CPU model and the BLAS library."""
+    cores, blas = 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            cores = max(i["num_threads"] for i in libs)
+            blas = "%s %s" % (libs[0].get("internal_api"), libs[0].get("version"))
+    except Exception:  # pragma: no cover
+        pass
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return int(cores), model, blas
+
+
+def prefill_sample_rows(L, k, count, seed=0):
+    """Deterministic oracle sample of a long causal prefill: the rows at the
+    ends and around the k boundary (0, 1, k-2, k-1, k, k+1, L-1), plus one
+    seeded row in each of count-7 equal strata of [0, L)."""
+    fixed = sorted({r for r in (0, 1, k - 2, k - 1, k, k + 1, L - 1) if 0 <= r < L})
+    n_strata = max(count - len(fixed), 0)
+    rng = np.random.default_rng(seed)
+    edges = np.linspace(0, L, n_strata + 1).astype(np.int64)
+    strat = [int(rng.integers(edges[i], max(edges[i + 1], edges[i] + 1))) for i in range(n_strata)]
+    return fixed, strat
+
+
+def cpu_baseline(wl, synth_obj, budget_s, sample_rows=256):
+    """The oracle as it stands, timed on this host over a bounded sample.
+
+    Long prefills (more than 16384 rows): the fixed + stratified rows of
+    prefill_sample_rows, each stage timed apart; the indexer and top-k times
+    scale to every row by sum(t + 1) (the candidates), the attention time by
+    sum(min(k, t + 1)) (the selected rows).  Other workloads: rows in order
+    (decode) or a seeded permutation (prefill), each row repeated until its
+    share of budget_s is spent.  Regenerating a row's inputs is never timed."""
     from oracle import dsa_oracle as O
     lay = synth_obj.layout
     rows = O.query_rows(lay.q_seq_start, lay.k_len)
+    cores, model, blas = host_info()
+    host = {"cores": cores, "cpu_model": model, "blas": blas}
+    dec = (lambda c, s: O.dequant_e4m3(c, s)) if wl.fp8 else (lambda c, s: c.astype(np.float64))
+    dec_bf = O.decode_bf16 if wl.fp8 else (lambda x: x.astype(np.float64))
+
+    if wl.kind == "prefill" and len(rows) > 16384:
+        L, k = len(rows), wl.top_k
+        fixed, strat = prefill_sample_rows(L, k, sample_rows)
+        sample = sorted(set(fixed) | set(strat))
+        kc, ks = synth_obj.ki(0, L)
+        keys = dec(kc, ks)
+        kv = dec_bf(synth_obj.kv(0, L))
+        # every sampled row's inputs first (each regenerates its 256-row chunk,
+        # so the rows are drawn in parallel), then the timed oracle calls
+        from concurrent.futures import ThreadPoolExecutor
+
+        def inputs(t):
+            qc, qs = synth_obj.qi(t, t + 1)
+            return dec(qc, qs)[0], synth_obj.w(t, t + 1)[0], dec_bf(synth_obj.q(t, t + 1))[0]
+
+        with ThreadPoolExecutor(min(16, max(cores, 1))) as ex:
+            row_in = dict(zip(sample, ex.map(inputs, sample)))
+        t_sel = t_att = 0.0
+        for t in sample:
+            n = rows[t][2]
+            qi_h, w, q_h = row_in.pop(t)
+            t0 = time.perf_counter()
+            sc = O.indexer_scores(qi_h, w, keys[:n], wl.index_scale)
+            idx = O.topk_indices(sc, k)
+            t1 = time.perf_counter()
+            O.sparse_mla(q_h, kv[:n], idx, wl.d_v, wl.sm_scale)
+            t2 = time.perf_counter()
+            t_sel += t1 - t0
+            t_att += t2 - t1
+        n_all = np.arange(1, L + 1, dtype=np.float64)
+        n_smp = np.array([rows[t][2] for t in sample], dtype=np.float64)
+        f_sel = n_all.sum() / n_smp.sum()
+        f_att = np.minimum(n_all, k).sum() / np.minimum(n_smp, k).sum()
+        total = t_sel * f_sel + t_att * f_att
+        return dict(host, value=L / total, unit="query-tokens/s", kind="oracle", extrapolated=True,
+                    sample="%d of %d query rows of %s (rows %s, plus one seeded row in each of %d equal strata); "
+                           "indexer + top-k time %.2f s scaled by sum(t+1) (x%.1f), attention time %.2f s "
+                           "scaled by sum(min(k, t+1)) (x%.1f): extrapolated %.0f s for all rows; float64 numpy"
+                           % (len(sample), L, wl.name, fixed, len(strat), t_sel, f_sel, t_att, f_att, total))
+
     order = list(range(len(rows)))
     if wl.kind == "prefill":  # spread the sample over the causal range
-        rng = np.random.default_rng(0)
-        order = list(rng.permutation(len(rows)))
+        order = list(np.random.default_rng(0).permutation(len(rows)))
     done = rows_seen = 0
-    elapsed = 0.0  # oracle time only; regenerating a row's inputs is not timed
+    elapsed = 0.0
     # Each row's inputs are generated once and its oracle call repeats until
     # the row's share of the budget is spent, so a workload of few rows (32
     # decodes) still gets a sample of about budget_s seconds.
@@ -145,19 +250,14 @@ def cpu_baseline(wl, synth_obj, budget_s):
     for t in order:
         b, p, n = rows[t]
         base = int(lay.k_seq_start[b])
-        qi, qs = synth_obj.qi(t, t + 1)
-        ki, ks = synth_obj.ki(base, base + n)
-        q = synth_obj.q(t, t + 1)
-        kv = synth_obj.kv(base, base + n)
+        qc, qs = synth_obj.qi(t, t + 1)
+        kc, ks = synth_obj.ki(base, base + n)
+        qi_h, ki_h = dec(qc, qs)[0], dec(kc, ks)
+        q_h, kv_h = dec_bf(synth_obj.q(t, t + 1))[0], dec_bf(synth_obj.kv(base, base + n))
         w = synth_obj.w(t, t + 1)[0]
         row_time = 0.0
         while True:
             t0 = time.perf_counter()
-            if wl.fp8:
-                qi_h, ki_h = O.dequant_e4m3(qi, qs)[0], O.dequant_e4m3(ki, ks)
-                q_h, kv_h = O.decode_bf16(q)[0], O.decode_bf16(kv)
-            else:
-                qi_h, ki_h, q_h, kv_h = qi[0].astype(float), ki.astype(float), q[0].astype(float), kv.astype(float)
             O.forward_row(qi_h, w, ki_h, q_h, kv_h, n, wl.top_k, wl.index_scale, wl.d_v, wl.sm_scale)
             dt = time.perf_counter() - t0
             elapsed += dt
@@ -168,17 +268,11 @@ def cpu_baseline(wl, synth_obj, budget_s):
         rows_seen += 1
         if elapsed > budget_s:
             break
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = max(i["num_threads"] for i in blas) if blas else 1
-    except Exception:  # pragma: no cover
-        cores = 1
-    return {"value": done / elapsed, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "%d oracle calls over %d of %d query rows of %s (%s), each the full path: indexer over "
-                      "all n_t keys, top-k, sparse MLA; float64 numpy; %.1f s of oracle time" % (
-                          done, rows_seen, len(rows), wl.name, "first rows" if wl.kind != "prefill" else "random rows",
-                          elapsed)}
+    return dict(host, value=done / elapsed, unit="query-tokens/s", kind="oracle", extrapolated=False,
+                sample="%d oracle calls over %d of %d query rows of %s (%s), each the full path: indexer over "
+                       "all n_t keys, top-k, sparse MLA; float64 numpy; %.1f s of oracle time" % (
+                           done, rows_seen, len(rows), wl.name,
+                           "first rows" if wl.kind != "prefill" else "random rows", elapsed))
 
 
 # --------------------------------------------------------------------------
@@ -452,45 +546,21 @@ def bench_module_forward(args):
         "cpu_baseline": cpu}))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the path has no multi-GPU form in this library "
-              "(got --gpus %d)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def measure(wl, steps, warmup, copies, dev, log):
+    """Times one workload on the GPU: the dsa_forward loop (the step), the
+    stage-by-stage loop (each stage's duration), and where dsa_forward takes
+    the fused indexer -> top-k kernel, that call alone.  Returns the figures
+    of the line (everything but the CPU baseline) and the device workload."""
     import torch
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-    if args.op == "cache_append":
-        bench_cache_append(args)
-        return
-    if args.op == "output_projection":
-        bench_output_projection(args)
-        return
-    if args.op == "module_forward":
-        bench_module_forward(args)
-        return
     from sparse_attention_long_fp8_amd import binding as B
-    from sparse_attention_long_fp8_amd import synth
     from sparse_attention_long_fp8_amd.workload import DeviceWorkload
 
-    wl = synth.WORKLOADS[args.workload]
     decode = wl.kind != "prefill"
-    steps = args.steps if args.steps is not None else (200 if decode else 10)
-    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
-    copies = args.copies if args.copies is not None else (4 if decode else 1)
-    dev = torch.device("cuda:0")
-    B.lib()  # fail loudly now if the library is missing
-
-    def log(msg):
-        print("[bench] " + msg, file=sys.stderr, flush=True)
-
     dw = DeviceWorkload(wl, dev, copies=copies, log=log)
     lay, T = dw.lay, dw.T
     stream = torch.cuda.current_stream()
 
-    log("warmup %d, timed %d steps, %d input copies" % (warmup, steps, copies))
+    log("%s: warmup %d, timed %d steps, %d input copies" % (wl.name, warmup, steps, copies))
     dw.prepare_forward()
     for i in range(warmup):
         dw.forward_prepared(i, stream)
@@ -506,11 +576,10 @@ def main():
         dw.forward_prepared(warmup + i, stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    ms_step = total_ms / steps
+    ms_step = t_begin.elapsed_time(t_end) / steps
     # Per-kernel durations: the same passes stage by stage with HIP events
     # recorded around each stage on the launch stream (the event records add
-    # a few microseconds between stages, so this loop does not give `value`).
+    # a few microseconds between stages, so this loop does not give the step).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -522,8 +591,8 @@ def main():
         "mla": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
     }
     # Where dsa_forward takes the fused indexer -> top-k kernel (prefill), time
-    # that call too: it replaces the first two stages inside `value`.
-    fused = wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and not wl.paged and lay.max_q_per_seq >= 8
+    # that call too: it replaces the first two stages inside the step.
+    fused = fused_applies(wl, lay)
     if fused:
         qi0, qs0, w0, _, ki0, ks0, _ = dw.sets[0]
         nb = B.dsa_indexer_topk_workspace_size(dw.batch, dw.layout, dw.index_dtype, wl.h_i, wl.d_i, wl.top_k)
@@ -558,48 +627,136 @@ def main():
             ach = wk["flops"] / t_s
             rooflines[st_name] = {"bound": "mfma", "achieved": ach / 1e12, "peak": wk["peak_flops"] / 1e12,
                                   "unit": "TFLOP/s", "frac": ach / wk["peak_flops"]}
-        tr = traffic_of(st_name, wl.name)
-        rooflines[st_name]["traffic"] = tr
+        rooflines[st_name]["traffic"] = traffic_of(st_name, wl.name)
         rooflines[st_name]["kernel"] = kernel_name(st_name, wl, lay)
         rooflines[st_name]["us"] = stage_ms[st_name] * 1e3
-    dominant = max(stage_ms, key=stage_ms.get)
-    # The path's own fraction over indexer + attention, top-k reported apart
-    # (the stage-by-stage loop's times): decode, algorithmic bytes of both
-    # against HBM; prefill, both stages' flops each at its own dtype's peak.
-    t_path = (stage_ms["indexer"] + stage_ms["mla"]) / 1e3
+    # The kernels the step runs: with the fused kernel, indexer_topk replaces
+    # the indexer and top-k stages.
+    in_step = ["indexer_topk", "mla"] if fused else ["indexer", "topk", "mla"]
+    dominant = max(in_step, key=stage_ms.get)
+    # The path's own fraction over indexer + attention (decode: algorithmic
+    # bytes of both against HBM, top-k apart; prefill: both stages' flops each
+    # at its own dtype's peak).  With the fused kernel the indexer time is the
+    # fused call's, which includes the selection.
+    t_ix = stage_ms["indexer_topk"] if fused else stage_ms["indexer"]
+    t_path = (t_ix + stage_ms["mla"]) / 1e3
     if decode:
         path = {"bound": "hbm", "frac": (work["indexer"]["bytes"] + work["mla"]["bytes"]) / HBM_PEAK / t_path,
                 "definition": "(indexer bytes + attention bytes) / (8 TB/s x (t_indexer + t_attention))"}
     else:
-        path = {"bound": "mfma", "frac": (work["indexer"]["flops"] / work["indexer"]["peak_flops"]
-                                          + work["mla"]["flops"] / work["mla"]["peak_flops"]) / t_path,
-                "definition": "(indexer flops / its peak + attention flops / its peak) / (t_indexer + t_attention)"}
+        f_ideal = work["indexer"]["flops"] / work["indexer"]["peak_flops"] + work["mla"]["flops"] / work["mla"]["peak_flops"]
+        path = {"bound": "mfma", "frac": f_ideal / t_path,
+                "definition": ("(indexer flops / FP8 peak + attention flops / bf16 peak) / (t_indexer_topk "
+                               "+ t_attention): the fused indexer -> top-k call as the step runs it")
+                if fused else "(indexer flops / its peak + attention flops / its peak) / (t_indexer + t_attention)"}
+        if fused:
+            path["unfused_frac"] = f_ideal / ((stage_ms["indexer"] + stage_ms["mla"]) / 1e3)
     path["us"] = t_path * 1e6
-    result = {
-        "metric": METRIC,
+    fig = {
         "value": T / (ms_step / 1e3),
-        "unit": "query-tokens/s",
-        "n_gpus": 1,
+        "ms_per_step": ms_step,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "decode_us_per_step": ms_step * 1e3 if decode else None,
         "dtype": "fp8_e4m3+bf16" if wl.fp8 else "f32",
-        "data": "synthetic",
         "config": {"workload": wl.name, "queries": T, "batch": wl.batch, "kind": wl.kind,
                    "max_ctx": lay.max_k_len, "top_k": wl.top_k, "h_i": wl.h_i, "d_i": wl.d_i,
                    "heads": wl.heads, "d_qk": wl.d_qk, "d_v": wl.d_v, "paged": wl.paged,
+                   "needles": wl.needles, "drift_block": wl.drift_block, "seed": wl.seed,
                    "input_copies": copies},
-        "decode_us_per_step": ms_step * 1e3 if decode else None,
         "roofline": dict(rooflines[dominant]),
         "stages": rooflines,
         "path_roofline": path,
     }
+    return fig, dw
+
+
+def default_counts(wl, steps, warmup, copies):
+    decode = wl.kind != "prefill"
+    return (steps if steps is not None else (200 if decode else 10),
+            warmup if warmup is not None else (20 if decode else 3),
+            copies if copies is not None else (4 if decode else 1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU form in this library "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.op == "cache_append":
+        bench_cache_append(args)
+        return
+    if args.op == "output_projection":
+        bench_output_projection(args)
+        return
+    if args.op == "module_forward":
+        bench_module_forward(args)
+        return
+    from sparse_attention_long_fp8_amd import binding as B
+    from sparse_attention_long_fp8_amd import synth
+
+    dev = torch.device("cuda:0")
+    B.lib()  # fail loudly now if the library is missing
+
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    wl = synth.WORKLOADS[args.workload]
+    steps, warmup, copies = default_counts(wl, args.steps, args.warmup, args.copies)
+    fig, dw = measure(wl, steps, warmup, copies, dev, log)
+    synth_obj = dw.synth
+    del dw
+    torch.cuda.empty_cache()
+    result = {
+        "metric": METRIC,
+        "value": fig["value"],
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": fig["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": fig["dtype"],
+        "data": "synthetic",
+        "config": fig["config"],
+        "decode_us_per_step": fig["decode_us_per_step"],
+        "roofline": fig["roofline"],
+        "stages": fig["stages"],
+        "path_roofline": fig["path_roofline"],
+    }
+    # The other workloads, each built, timed and freed in turn.  They run the
+    # headline's step count (decode: at least 100 steps, since a step is
+    # about 0.1 ms) and their own warm-up and input-copy defaults.
+    others = [] if args.others == "none" else (
+        [w for w in ALL_WORKLOADS if w != wl.name] if args.others == "all" else
+        [w for w in args.others.split(",") if w and w != wl.name])
+    table = {}
+    for name in others:
+        owl = synth.WORKLOADS[name]
+        o_steps = steps if owl.kind == "prefill" else max(steps, 100)
+        o_steps, o_warm, o_copies = default_counts(owl, o_steps, None, None)
+        ofig, odw = measure(owl, o_steps, o_warm, o_copies, dev, log)
+        del odw
+        torch.cuda.empty_cache()
+        table[name] = {
+            "ms_per_step": ofig["ms_per_step"], "query_tokens_per_s": ofig["value"],
+            "decode_us_per_step": ofig["decode_us_per_step"], "steps": o_steps, "warmup": o_warm,
+            "dtype": ofig["dtype"], "config": ofig["config"],
+            "stages": {k: {"us": v["us"], "frac": v["frac"], "bound": v["bound"], "kernel": v["kernel"],
+                           "traffic": v["traffic"]} for k, v in ofig["stages"].items()},
+            "path_roofline": ofig["path_roofline"],
+        }
+    result["workloads"] = table
     if not args.no_cpu_baseline:
-        print("[bench] CPU oracle baseline (budget %.0f s)" % args.cpu_budget, file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, dw.synth, args.cpu_budget)
+        log("CPU oracle baseline on %s" % wl.name)
+        result["cpu_baseline"] = cpu_baseline(wl, synth_obj, args.cpu_budget, args.cpu_sample)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

@@ -283,33 +283,6 @@ dsa_status_t dsa_cache_append(const dsa_kv_layout_t *layout, int32_t num_tokens,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Output projections after the sparse stage ([G] Stage 2, the u_t equation;
- * the implementation section's w_uv and w_out linear layers):
- *
- *   y[t, h, :] = W_UV,h . o[t, h, :]          (d_c -> d_h, per head)
- *   out[t, :]  = W_O . concat_h y[t, h, :]      (heads * d_h -> hidden)
- *
- * Both are dense bf16 GEMMs with fp32 accumulation, run by hipBLASLt; y is
- * rounded to bf16 in the workspace between them.
- *   blaslt  a hipBLASLt handle (dsa_blaslt_create, or the caller's own
- *           hipblasLtCreate), used on `stream`
- *   o       [T, heads, d_c] bf16 (dsa_sparse_mla_fwd's output)
- *   w_uv    [heads * d_h, d_c] bf16 (rows h*d_h .. are W_UV,h)
- *   w_o     [hidden, heads * d_h] bf16
- *   out     [T, hidden] bf16
- *   d_c, d_h, hidden: multiples of 8.  workspace: 256-byte aligned,
- *   dsa_output_projection_workspace_size() bytes (y, then 32 MiB for the
- *   GEMM library).
- * ---------------------------------------------------------------------- */
-dsa_status_t dsa_output_projection(void *blaslt, int32_t num_queries, int32_t heads, int32_t d_c,
-                                   int32_t d_h, int32_t hidden, const void *o, const void *w_uv,
-                                   const void *w_o, void *out, void *workspace,
-                                   size_t workspace_bytes, hipStream_t stream);
-
-dsa_status_t dsa_output_projection_workspace_size(int32_t num_queries, int32_t heads, int32_t d_h,
-                                                  size_t *bytes);
-
-/* ------------------------------------------------------------------------
  * The page's complete DSA module ([G] "End-to-End Implementation": the
  * DeepSeekSparseAttention module with its LightningIndexer), fp32, one query
  * token per batch element over a history of seq_len tokens:
@@ -351,11 +324,6 @@ dsa_status_t dsa_module_forward_workspace_size(int32_t batch, int32_t seq_len, i
                                                int32_t heads, int32_t head_dim,
                                                int32_t latent_dim, int32_t index_dim,
                                                size_t *bytes);
-
-/* A hipBLASLt handle for dsa_output_projection (host and device resources
- * of the GEMM library; the caller owns it and destroys it). */
-dsa_status_t dsa_blaslt_create(void **handle);
-dsa_status_t dsa_blaslt_destroy(void *handle);
 
 /* ------------------------------------------------------------------------
  * Precondition check on request.  The entry points above validate their

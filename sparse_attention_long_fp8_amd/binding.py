@@ -16,7 +16,9 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdsa.so")
+PROJ_LIB_PATH = os.path.join(PKG, "libdsa_proj.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "libdsa.h")
+PROJ_HEADER = os.path.join(os.path.dirname(PKG), "include", "libdsa_proj.h")
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = range(3)
@@ -73,23 +75,27 @@ _SIGS = {
                                         c_i32, c_i32, ctypes.POINTER(c_size)],
     "dsa_cache_append": [ctypes.POINTER(dsa_kv_layout_t), c_i32, c_ptr, c_ptr, c_i32, c_ptr, c_ptr, c_ptr,
                          c_i32, c_ptr, c_ptr, c_ptr],
-    "dsa_output_projection": [c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size,
-                              c_ptr],
-    "dsa_output_projection_workspace_size": [c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
     "dsa_module_forward": [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32] + [c_ptr] * 11
                           + [c_ptr, c_size, c_ptr],
     "dsa_module_forward_workspace_size": [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                           ctypes.POINTER(c_size)],
-    "dsa_blaslt_create": [ctypes.POINTER(c_ptr)],
-    "dsa_blaslt_destroy": [c_ptr],
     "dsa_status_string": [c_i32],
     "dsa_last_error": [],
     "dsa_abi_version": [],
+}
+# libdsa_proj.so (include/libdsa_proj.h): the hipBLASLt output projections
+_PROJ_SIGS = {
+    "dsa_output_projection": [c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_size,
+                              c_ptr],
+    "dsa_output_projection_workspace_size": [c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
+    "dsa_blaslt_create": [ctypes.POINTER(c_ptr)],
+    "dsa_blaslt_destroy": [c_ptr],
 }
 _RESTYPES = {"dsa_status_string": ctypes.c_char_p, "dsa_last_error": ctypes.c_char_p,
              "dsa_abi_version": c_i32}
 
 _LIB = None
+_PROJ_LIB = None
 
 
 def lib():
@@ -108,9 +114,27 @@ def lib():
     return _LIB
 
 
-def header_functions():
-    """Names of the functions include/libdsa.h declares."""
-    text = open(HEADER).read()
+def proj_lib():
+    """The loaded libdsa_proj.so, the output projections (raises if it has
+    not been built).  It links hipBLASLt; libdsa.so does not."""
+    global _PROJ_LIB
+    if _PROJ_LIB is None:
+        lib()  # its status helpers live in libdsa.so
+        if not os.path.exists(PROJ_LIB_PATH):
+            raise RuntimeError("libdsa_proj.so not found at %s; build it with "
+                               "`python -m sparse_attention_long_fp8_amd.build`" % PROJ_LIB_PATH)
+        handle = ctypes.CDLL(PROJ_LIB_PATH)
+        for name, args in _PROJ_SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = c_i32
+        _PROJ_LIB = handle
+    return _PROJ_LIB
+
+
+def header_functions(header=HEADER):
+    """Names of the functions a header (default include/libdsa.h) declares."""
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:dsa_status_t|const char \*|int32_t)\s*(dsa_\w+)\s*\(", text, re.M)))
 
 
@@ -274,24 +298,24 @@ def dsa_cache_append(layout, num_tokens, seq, pos, d_i, k_new, k_pool, k_scale_p
 
 def dsa_blaslt_create():
     h = c_ptr()
-    _check(lib().dsa_blaslt_create(ctypes.byref(h)), "dsa_blaslt_create")
+    _check(proj_lib().dsa_blaslt_create(ctypes.byref(h)), "dsa_blaslt_create")
     return h.value
 
 
 def dsa_blaslt_destroy(handle):
-    _check(lib().dsa_blaslt_destroy(handle), "dsa_blaslt_destroy")
+    _check(proj_lib().dsa_blaslt_destroy(handle), "dsa_blaslt_destroy")
 
 
 def dsa_output_projection_workspace_size(num_queries, heads, d_h):
     n = c_size(0)
-    _check(lib().dsa_output_projection_workspace_size(int(num_queries), int(heads), int(d_h), ctypes.byref(n)),
+    _check(proj_lib().dsa_output_projection_workspace_size(int(num_queries), int(heads), int(d_h), ctypes.byref(n)),
            "dsa_output_projection_workspace_size")
     return n.value
 
 
 def dsa_output_projection(blaslt, num_queries, heads, d_c, d_h, hidden, o, w_uv, w_o, out, workspace,
                           workspace_bytes, stream=None, check=True):
-    st = lib().dsa_output_projection(blaslt, int(num_queries), int(heads), int(d_c), int(d_h), int(hidden), _p(o),
+    st = proj_lib().dsa_output_projection(blaslt, int(num_queries), int(heads), int(d_c), int(d_h), int(hidden), _p(o),
                                      _p(w_uv), _p(w_o), _p(out), _p(workspace), int(workspace_bytes),
                                      _stream(stream))
     if check:

@@ -1,4 +1,5 @@
-"""Build libdsa.so (and the test-only MFMA probe library) for gfx950 with hipcc.
+"""Build libdsa.so, libdsa_proj.so (the hipBLASLt output projections) and the
+test-only MFMA probe library for gfx950 with hipcc.
 
 Usage: python -m sparse_attention_long_fp8_amd.build [-v]
 The libraries are written next to this file, so they travel with the tree.
@@ -25,9 +26,11 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "module.hip", "validate.hip",
-               "libdsa.cpp", "projection.cpp", "module.cpp"]
-# the output projections are plain GEMMs, run by hipBLASLt
-LIB_LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+               "libdsa.cpp", "module.cpp"]
+# the output projections are plain GEMMs, run by hipBLASLt, in a library of
+# their own (libdsa_proj.so) so that libdsa.so loads no GEMM library
+PROJ_SOURCES = ["projection.cpp"]
+PROJ_LINK = ["-L" + PKG, "-ldsa", "-Wl,-rpath,$ORIGIN", "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 # Per-source flags.  The FP8 indexer reads every MFMA result with VALU code
 # (ReLU, head weights); keeping the accumulators in ordinary VGPRs saves one
@@ -36,6 +39,7 @@ SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 PROBE_SOURCES = ["probe.hip"]
 
 LIB_PATH = os.path.join(PKG, "libdsa.so")
+PROJ_PATH = os.path.join(PKG, "libdsa_proj.so")
 PROBE_PATH = os.path.join(PKG, "libdsa_probe.so")
 
 
@@ -93,11 +97,12 @@ def _link(objs, out, verbose, libs=()):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link both libraries; returns libdsa.so's path."""
-    srcs = LIB_SOURCES + PROBE_SOURCES
+    """Compile every source and link the three libraries; returns libdsa.so's path."""
+    srcs = LIB_SOURCES + PROJ_SOURCES + PROBE_SOURCES
     with ThreadPoolExecutor(min(len(srcs), 8)) as ex:
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
-    _link([objs[s] for s in LIB_SOURCES], LIB_PATH, verbose, LIB_LINK)
+    _link([objs[s] for s in LIB_SOURCES], LIB_PATH, verbose)
+    _link([objs[s] for s in PROJ_SOURCES], PROJ_PATH, verbose, PROJ_LINK)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_PATH, verbose)
     return LIB_PATH
 

@@ -296,8 +296,6 @@ dsa_status_t dsa_validate(const dsa_batch_t *batch, const dsa_kv_layout_t *layou
 
 dsa_status_t dsa_topk(const dsa_batch_t *batch, const float *scores, int64_t ld_scores, int32_t k, int32_t *indices,
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   dsa_status_t st = check_topk(batch, scores, ld_scores, k, indices);
   if (st != DSA_OK) return st;
   const size_t need = dsa::topk_workspace_bytes(batch->num_queries, batch->max_k_len, k);

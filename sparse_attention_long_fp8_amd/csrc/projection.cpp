@@ -20,7 +20,7 @@
 #include <cstdio>
 #include <string>
 
-#include "libdsa.h"
+#include "libdsa_proj.h"
 
 namespace {
 

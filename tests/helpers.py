@@ -163,17 +163,33 @@ def check_indexer(case, scores_gpu, rows):
     """Indexer parity on the given rows; returns the oracle scores by row."""
     got_all = scores_gpu.cpu().numpy()
     refs = {}
+    worst = 0.0
     for t in rows:
         b, p, n = case.rows[t]
         ref = case.ref_scores(t)
         got = got_all[t, :n].astype(np.float64)
         assert not np.isnan(got).any(), "row %d: unwritten or NaN scores" % t
-        tol = IDX_RTOL * np.abs(ref) + IDX_FLOOR * np.abs(ref).max()
-        bad = np.abs(got - ref) > tol
-        assert not bad.any(), "row %d: %d scores off, worst |d|=%g at s=%d (ref %g)" % (
-            t, bad.sum(), np.abs(got - ref).max(), int(np.argmax(np.abs(got - ref))), ref[np.argmax(np.abs(got - ref))])
+        worst = max(worst, indexer_margin(got, ref, t))
         refs[t] = ref
+    report("indexer", case.wl.name, worst)
     return refs
+
+
+def indexer_margin(got, ref, t):
+    """Worst |I_gpu - I_ref| / tolerance of one row (asserts it is <= 1)."""
+    tol = IDX_RTOL * np.abs(ref) + IDX_FLOOR * np.abs(ref).max()
+    d = np.abs(got - ref)
+    bad = d > tol
+    assert not bad.any(), "row %d: %d scores off, worst |d|=%g at s=%d (ref %g)" % (
+        t, bad.sum(), d.max(), int(np.argmax(d)), ref[np.argmax(d)])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(tol > 0, d / tol, 0.0)
+    return float(r.max()) if r.size else 0.0
+
+
+def report(what, case, ratio):
+    """Prints the worst error / tolerance ratio of a parity check (pytest -s shows it)."""
+    print("[margin] %s %s: worst error / tolerance = %.3g" % (what, case, ratio), flush=True)
 
 
 def check_topk_exact(case, scores_gpu, idx_gpu, rows, k=None):
@@ -210,7 +226,7 @@ def check_mla(case, idx_gpu, out_gpu, lse_gpu, rows, tol=None):
     i_all = idx_gpu.cpu().numpy()
     o_all = out_gpu.float().cpu().numpy()
     l_all = lse_gpu.cpu().numpy()
-    worst = 0.0
+    worst = worst_lse = 0.0
     for t in rows:
         b, p, n = case.rows[t]
         o_ref, lse_ref = O.sparse_mla(case.q_hat[t], case.seq_kv(b)[:n], i_all[t], case.wl.d_v, case.wl.sm_scale)
@@ -219,6 +235,9 @@ def check_mla(case, idx_gpu, out_gpu, lse_gpu, rows, tol=None):
         err = np.abs(o - o_ref).max() / max(np.abs(o_ref).max(), 1e-30)
         worst = max(worst, err)
         assert err <= tol, "row %d: attention error %g > %g" % (t, err, tol)
-        assert np.abs(l_all[t] - lse_ref).max() <= LSE_TOL, "row %d: lse off by %g" % (
-            t, np.abs(l_all[t] - lse_ref).max())
+        dl = np.abs(l_all[t] - lse_ref).max()
+        worst_lse = max(worst_lse, dl)
+        assert dl <= LSE_TOL, "row %d: lse off by %g" % (t, dl)
+    report("attention", case.wl.name, worst / tol)
+    report("lse", case.wl.name, worst_lse / LSE_TOL)
     return worst

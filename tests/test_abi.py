@@ -21,9 +21,24 @@ def _layout(rows=8):
 def test_exports_match_header():
     lib = B.lib()
     names = B.header_functions()
-    assert len(names) == 20
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_projection_library_exports_and_keeps_blaslt_out_of_libdsa():
+    proj = B.proj_lib()
+    names = B.header_functions(B.PROJ_HEADER)
+    assert names == ["dsa_blaslt_create", "dsa_blaslt_destroy", "dsa_output_projection",
+                     "dsa_output_projection_workspace_size"]
+    for name in names:
+        assert hasattr(proj, name), name
+    # the hot-path library does not link the GEMM library
+    import subprocess
+    deps = subprocess.run(["readelf", "-d", B.LIB_PATH], capture_output=True, text=True).stdout
+    assert "hipblaslt" not in deps.lower()
+    assert "hipblaslt" in subprocess.run(["readelf", "-d", B.PROJ_LIB_PATH], capture_output=True,
+                                         text=True).stdout.lower()
 
 
 def test_version_and_strings():

@@ -72,3 +72,21 @@ def test_more_than_one_gpu_is_refused(n):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
+
+
+def test_prefill_oracle_sample():
+    # the fixed rows (ends and the k boundary) plus one seeded row per stratum,
+    # deterministic and inside [0, L)
+    fixed, strat = bench.prefill_sample_rows(65536, 2048, 256)
+    assert fixed == [0, 1, 2046, 2047, 2048, 2049, 65535]
+    assert len(strat) == 249 and all(0 <= r < 65536 for r in strat)
+    edges = [int(x) for x in __import__("numpy").linspace(0, 65536, 250)]
+    assert all(edges[i] <= r < edges[i + 1] for i, r in enumerate(strat))
+    assert (fixed, strat) == bench.prefill_sample_rows(65536, 2048, 256)
+    assert len(set(fixed) | set(strat)) >= 250
+
+
+def test_headline_is_the_long_prefill():
+    # the default line measures the largest single-GPU workload
+    assert bench.HEADLINE == "prefill_64k"
+    assert set(bench.ALL_WORKLOADS) == set(synth.WORKLOADS)

@@ -10,6 +10,7 @@ import torch
 
 from oracle import dsa_oracle as O
 from sparse_attention_long_fp8_amd import synth
+from bench import prefill_sample_rows
 from sparse_attention_long_fp8_amd.workload import DeviceWorkload
 from tests import helpers as H
 
@@ -19,19 +20,14 @@ FULL = ["decode_32k", "prefill_16k", "prefill_64k", "paged_decode"]
 
 
 def _sample(wl, rows):
+    """Every row of the decode workloads; on the prefills the rows at the ends
+    and around the k boundary plus seeded rows in equal strata (the 64k
+    prefill: the benchmark's 256-row oracle sample)."""
     T = len(rows)
-    rng = np.random.default_rng(123)
-    if wl.name == "decode_32k":
-        return list(range(T))
     if wl.kind == "decode":
-        n = np.array([r[2] for r in rows])
-        pick = {int(n.argmin()), int(n.argmax())}
-        pick |= set(rng.choice(T, 10, replace=False).tolist())
-        return sorted(pick)
-    k = wl.top_k
-    edge = {0, 1, k - 2, k - 1, k, k + 1, T - 1}
-    extra = 25 if T <= 16384 else 9
-    return sorted(edge | set(rng.choice(T, extra, replace=False).tolist()))
+        return list(range(T))
+    fixed, strat = prefill_sample_rows(T, wl.top_k, 256 if T > 16384 else 64, seed=123)
+    return sorted(set(fixed) | set(strat))
 
 
 class RowOracle:
@@ -53,12 +49,29 @@ class RowOracle:
             self._seq[b] = (O.dequant_e4m3(kc, ks), O.decode_bf16(self.s.kv(base, base + n)))
         return self._seq[b]
 
+    def prefetch(self, rows):
+        """Regenerates the query-side inputs of `rows` in parallel (each row
+        redraws its 256-row chunk, so one at a time is slow)."""
+        from concurrent.futures import ThreadPoolExecutor
+
+        def one(t):
+            qc, qs = self.s.qi(t, t + 1)
+            return (O.dequant_e4m3(qc, qs)[0], self.s.w(t, t + 1)[0].astype(np.float64),
+                    O.decode_bf16(self.s.q(t, t + 1))[0])
+
+        with ThreadPoolExecutor(16) as ex:
+            self._q = dict(zip(rows, ex.map(one, rows)))
+
     def row(self, t):
         b, p, n = self.rows[t]
-        qc, qs = self.s.qi(t, t + 1)
+        if t in getattr(self, "_q", {}):
+            qi_h, w, q_h = self._q.pop(t)
+        else:
+            qc, qs = self.s.qi(t, t + 1)
+            qi_h, w, q_h = (O.dequant_e4m3(qc, qs)[0], self.s.w(t, t + 1)[0].astype(np.float64),
+                            O.decode_bf16(self.s.q(t, t + 1))[0])
         keys, kv = self.seq(b)
-        return (O.dequant_e4m3(qc, qs)[0], self.s.w(t, t + 1)[0].astype(np.float64), keys[:n],
-                O.decode_bf16(self.s.q(t, t + 1))[0], kv[:n], n)
+        return qi_h, w, keys[:n], q_h, kv[:n], n
 
 
 @pytest.fixture(scope="module", params=FULL)
@@ -103,16 +116,15 @@ def test_sampled_rows_match_oracle(full):
     ro = RowOracle(dw)
     rows = _sample(wl, ro.rows)
     print("[full] %s: oracle on %d rows" % (wl.name, len(rows)), flush=True)
+    ro.prefetch(rows)
     scores = dw.scores
     idx = dw.idx.cpu().numpy()
-    worst_att = 0.0
+    worst_att = worst_idx = worst_lse = 0.0
     for t in rows:
         qi_h, w, keys, q_h, kv, n = ro.row(t)
         ref = O.indexer_scores(qi_h, w, keys, wl.index_scale)
         got = scores[t, :n].double().cpu().numpy()
-        tol = H.IDX_RTOL * np.abs(ref) + H.IDX_FLOOR * np.abs(ref).max()
-        bad = np.abs(got - ref) > tol
-        assert not bad.any(), "row %d: %d indexer scores off (worst %g)" % (t, bad.sum(), np.abs(got - ref).max())
+        worst_idx = max(worst_idx, H.indexer_margin(got, ref, t))
         # top-k bit-exact on the GPU's own scores
         assert np.array_equal(idx[t].astype(np.int64), O.topk_indices(got, wl.top_k)), "row %d: top-k" % t
         # end to end: differences only at near-ties of the oracle's k-th score
@@ -128,8 +140,13 @@ def test_sampled_rows_match_oracle(full):
         err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
         worst_att = max(worst_att, err)
         assert err <= H.ATTN_TOL_BF16, "row %d: attention error %g" % (t, err)
-        assert np.abs(dw.lse[t].cpu().numpy() - lse_ref).max() <= H.LSE_TOL, "row %d: lse" % t
+        dl = np.abs(dw.lse[t].cpu().numpy() - lse_ref).max()
+        worst_lse = max(worst_lse, dl)
+        assert dl <= H.LSE_TOL, "row %d: lse" % t
     print("[full] %s: worst attention error %.3g" % (wl.name, worst_att), flush=True)
+    H.report("indexer", wl.name, worst_idx)
+    H.report("attention", wl.name, worst_att / H.ATTN_TOL_BF16)
+    H.report("lse", wl.name, worst_lse / H.LSE_TOL)
 
 
 def test_needles_are_selected(full):
