@@ -66,6 +66,14 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The lane index, computed where it is used: the compiler can neither hoist
+// nor share it, so no register holds it across a loop.
+__device__ __forceinline__ int opaque_lane_id() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 
 // 16-byte global -> LDS load for a whole wave: lane i's 16 bytes land at LDS
@@ -85,6 +93,24 @@ __device__ __forceinline__ void lds_dma16_at(const void *gaddr, uint32_t lds_byt
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(base), "v"(gaddr)
+      : "memory");
+}
+
+// The same 16-byte load from one wave-uniform base address: lane i's 16
+// bytes come from sbase + voff (voff a per-lane byte offset) and land at LDS
+// byte address lds_byte + 16 * i.  The base is held in scalar registers, so
+// the lanes' addresses cost no vector arithmetic.
+__device__ __forceinline__ void lds_dma16_sbase(const void *sbase, uint32_t voff, uint32_t lds_byte) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte);
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(voff), "s"(sbase)
       : "memory");
 }
 

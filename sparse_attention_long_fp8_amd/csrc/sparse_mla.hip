@@ -19,6 +19,12 @@ namespace dsa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// 2^x by the hardware exponential alone (v_exp_f32).  Results below 2^-126
+// come out as zero instead of denormals; softmax terms that small relative
+// to the running maximum change nothing, and the range fix-up exp2f adds
+// for them costs four vector instructions per call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // --------------------------------------------------------------------------
 // fp32 path (1 <= heads <= 64, d_v <= d_qk <= 256).
 //
@@ -358,18 +364,27 @@ __global__ __launch_bounds__(256) void mla_f32_combine_kernel(int heads, int d_v
 constexpr int kD = 576;
 constexpr int kDv = 512;
 constexpr int kKs = kD / 32;                   // 18 K-steps of the QK product
+constexpr int kKsLat = kDv / 32;               // 16 of them over the latent part
 constexpr int kNt = kDv / 16;                  // 32 output dim tiles
 constexpr int kBlk = 32;                       // selected tokens per tile
 constexpr int kMaxSlots = 2048;                // slots one workgroup resolves
 constexpr int kRowBytes = kD * 2;              // 1152
-constexpr int kRowSlots = kRowBytes / 16 + 2;  // 72 data chunks + 2 pad chunks
-constexpr int kRowStride = kRowSlots * 16;     // 1184-byte LDS row pitch (measured best)
-constexpr int kTileSlots = kBlk * kRowSlots;   // 2368 16-byte slots
-constexpr int kTileLoads = kTileSlots / 64;    // 37 wave-wide 1 KB loads per tile
-constexpr int kTileBytes = kTileLoads * 64 * 16;
+constexpr int kLatBytes = kDv * 2;             // 1024: one wave-wide 16-byte load
+constexpr int kLatStride = kLatBytes + 16;     // LDS pitch of the latent parts
+constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128
+constexpr int kRopeOff = kBlk * kLatStride;    // rotary parts follow the latent parts
+constexpr int kTileBytes = kRopeOff + kBlk * kRopeBytes;
+constexpr int kRopeLoads = kBlk * kRopeBytes / 1024;  // 4: eight rows' rotary parts each
+constexpr int kTileLoads = kBlk + kRopeLoads;  // 36 wave-wide 1 KB loads per tile
 constexpr int kBufs = 4;                       // tile buffers: one computed, three in flight
 constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
-static_assert(kTileLoads * 64 == kTileSlots, "tile loads cover the tile exactly");
+#ifndef DSA_QK_AHEAD
+#define DSA_QK_AHEAD 2  // K-steps of A fragments read ahead of the QK MFMAs
+#endif
+#ifndef DSA_PV_AHEAD
+#define DSA_PV_AHEAD 3  // V fragments read ahead of the P.V MFMAs
+#endif
+static_assert(kRopeLoads * 8 == kBlk, "a rotary load covers eight rows");
 
 struct MlaLds {
   uint8_t tile[kBufs][kTileBytes];
@@ -457,23 +472,48 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   }
   lds_barrier();  // LDS only: the query loads stay in flight
 
-  // tile blk -> buffer buf: wave-wide load j of wave w fills LDS slots
-  // 64*(NW*j + w) .. +63; slot -> (row = slot / 74, chunk = slot % 74); chunks
-  // 72 and 73 are pitch padding (they reload chunk 0 of the row)
-  const bool hi = wave < kTileLoads % NW;
+  // tile blk -> buffer buf, in 36 wave-wide 1 KB loads:
+  //   * latent loads: the first 1024 bytes of row j of the tile go to LDS
+  //     offset j * kLatStride, all 64 lanes from that one row, so the row's
+  //     address is wave-uniform and lives in scalar registers; wave w takes
+  //     rows kBlk/NW * w .. + kBlk/NW - 1 (their resolved rows come in 16-byte
+  //     LDS reads);
+  //   * rotary loads: the last 128 bytes of rows 8q .. 8q+7 go to kRopeOff +
+  //     q * 1024, lane l taking row 8q + l/8; wave w takes q = w, w + NW, ...
+  //     Lane l's LDS position l % 8 of its row r holds rotary chunk
+  //     (l % 8) ^ (r % 8), so sixteen rows read at one chunk spread over the
+  //     LDS banks.
+  // Masked slots load row0 (their logits are discarded).
+  constexpr int kLatPer = kBlk / NW;
+  static_assert(kLatPer % 4 == 0, "latent rows come in groups of four");
+  const bool hi = wave < kTileLoads % NW;  // waves that issue kLHi loads a tile
   auto gather = [&](int blk, int buf) __attribute__((always_inline)) {
     const int32_t *rows = sh.rows + blk * kBlk;
-    const int nl = hi ? kLHi : kLLo;
-#pragma unroll 1
-    for (int j = 0; j < nl; ++j) {
-      const int base = 64 * (NW * j + wave);
-      const int slot = base + lane;
-      const int r = slot / kRowSlots;
-      int c = slot - r * kRowSlots;
-      int64_t row = rows[r];
-      if (row < 0) row = row0;
-      if (c >= kRowBytes / 16) c = 0;
-      lds_dma16_at(kv_bytes + row * kRowBytes + c * 16, lds_addr(&sh.tile[buf][0]) + base * 16);
+    const uint32_t tb = lds_addr(&sh.tile[buf][0]);
+#pragma unroll
+    for (int i0 = 0; i0 < kLatPer; i0 += 4) {
+      const int j0 = kLatPer * wave + i0;
+      const v4i r4 = *(const v4i *)(rows + j0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int row = __builtin_amdgcn_readfirstlane(r4[u]);
+        if (row < 0) row = (int)row0;
+        lds_dma16_sbase(kv_bytes + (int64_t)row * kRowBytes, 16u * lane, tb + (j0 + u) * kLatStride);
+      }
+    }
+#pragma unroll
+    for (int q0 = 0; q0 < kRopeLoads; q0 += NW) {
+      const int q = q0 + wave;
+      if (q < kRopeLoads) {
+        // the lane index is re-read here (two instructions) rather than kept:
+        // a loop-invariant address would be held in a register the tile loop
+        // does not have
+        const int ln = opaque_lane_id();
+        int row = rows[8 * q + (ln >> 3)];
+        if (row < 0) row = (int)row0;
+        lds_dma16_at(kv_bytes + (int64_t)row * kRowBytes + kLatBytes + 16 * ((ln & 7) ^ (ln >> 3)),
+                     tb + kRopeOff + q * 1024);
+      }
     }
   };
   // wait until at most `n` tiles of this wave's loads are still in flight
@@ -522,11 +562,16 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       s0[ht] = v4f{0.f, 0.f, 0.f, 0.f};
       s1[ht] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    const uint8_t *arow = tile + n16 * kRowStride + 16 * g;
+    // A fragments: K-steps 0-15 from the latent parts, 16-17 from the
+    // rotary parts (chunk c of row r at position c ^ (r % 8))
+    const uint8_t *alat = tile + n16 * kLatStride + 16 * g;
+    const uint8_t *arope = tile + kRopeOff + n16 * kRopeBytes;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      const v8bf a0 = *(const v8bf *)(arow + 64 * ks);
-      const v8bf a1 = *(const v8bf *)(arow + 16 * kRowStride + 64 * ks);
+      const int ro = 16 * ((4 * (ks - kKsLat) + g) ^ (n16 & 7));
+      const v8bf a0 = ks < kKsLat ? *(const v8bf *)(alat + 64 * ks) : *(const v8bf *)(arope + ro);
+      const v8bf a1 = ks < kKsLat ? *(const v8bf *)(alat + 16 * kLatStride + 64 * ks)
+                                  : *(const v8bf *)(arope + 16 * kRopeBytes + ro);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         s0[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ht][ks], s0[ht], 0, 0, 0);
@@ -534,13 +579,13 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       }
     }
     // keep two K-steps of A fragments (4 reads) ahead of the QK MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_QK_AHEAD, 1);
 #pragma unroll
-    for (int i = 0; i < kKs - 2; ++i) {
+    for (int i = 0; i < kKs - DSA_QK_AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * HT, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * HT, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * DSA_QK_AHEAD * HT, 1);
 
     // ---- online softmax (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
     bool ok[8];
@@ -552,27 +597,47 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     v8bf pf[HT];
     float alpha[HT];
     bool rescale = false;
+    float z[HT][8], xl[HT];
+    bool moves = false;  // some head's maximum may pass its reference by more than the slack
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      float z[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
-        z[4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
+        z[ht][i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
+        z[ht][4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
       }
-      float x = z[0];
+      xl[ht] = z[ht][0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) x = fmaxf(x, z[i]);
-      x = fmaxf(x, __shfl_xor(x, 16, 64));
-      x = fmaxf(x, __shfl_xor(x, 32, 64));
-      const float m_new = x > m_ref[ht] + kRefSlack ? x : m_ref[ht];
-      alpha[ht] = m_new == m_ref[ht] ? 1.f : exp2f(m_ref[ht] - m_new);
-      rescale |= alpha[ht] != 1.f;
-      m_ref[ht] = m_new;
+      for (int i = 1; i < 8; ++i) xl[ht] = fmaxf(xl[ht], z[ht][i]);
+      moves |= xl[ht] > m_ref[ht] + kRefSlack || m_ref[ht] == -INFINITY;
+    }
+    // A lane's own maximum decides: only if some lane's tile maximum passes
+    // its head's reference by more than the slack (or the head has no
+    // reference yet) does the wave take the heads' maxima across its lane
+    // groups and move the references.  Otherwise every term is exp2(z - m)
+    // with the reference kept, and no value crosses lanes.
+    if (__ballot(moves)) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float x = xl[ht];
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        const float m_new = x > m_ref[ht] + kRefSlack ? x : m_ref[ht];
+        alpha[ht] = m_new == m_ref[ht] ? 1.f : fast_exp2(m_ref[ht] - m_new);
+        rescale |= alpha[ht] != 1.f;
+        m_ref[ht] = m_new;
+      }
+    } else {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) alpha[ht] = 1.f;
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const float m = m_ref[ht];
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pv = m_new == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+        const float pv = m == -INFINITY ? 0.f : fast_exp2(z[ht][i] - m);
         sum += pv;
         pf[ht][i] = (__bf16)pv;
       }
@@ -595,11 +660,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
     // of a 16-dim tile); the transpose read hands lane i column i of the four
     // rows: 4 consecutive tokens of one dim, the B-operand slot order
-    const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kRowStride + 8 * (n16 & 3);
+    const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kRowStride + 32 * nt));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
       v8bf vb;
       __builtin_memcpy(&vb, &lo, 8);
       __builtin_memcpy((char *)&vb + 8, &hi, 8);
@@ -608,13 +673,13 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
         o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
     }
     // keep three V fragments (6 transpose reads) ahead of the PV MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_PV_AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < kNt - 3; ++i) {
+    for (int i = 0; i < kNt - DSA_PV_AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, HT, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3 * HT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, DSA_PV_AHEAD * HT, 0);
 
     // the next tile must have landed; the ones after it may stay in flight
     wait_tiles(min(nblk - 1, blk + kBufs - 1) - (blk + 1));
