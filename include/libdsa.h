@@ -35,8 +35,10 @@
  *   - Device-side preconditions are documented, not checked: batch arrays
  *     consistent with the host-side bounds, indices in range, page ids
  *     valid, no NaN scores.
- *   - The library keeps no mutable global state: calls on different streams
- *     (or threads) may run concurrently if their buffers do not overlap.
+ *   - The library keeps no mutable global state, except the static scratch
+ *     array of dsa_forward_noalloc: calls on different streams (or threads)
+ *     may run concurrently if their buffers do not overlap (for
+ *     dsa_forward_noalloc, see its note).
  *
  * Batch semantics.  Sequence b owns query rows q_seq_start[b] ..
  * q_seq_start[b+1]-1 and a key history of k_len[b] tokens.  Its nq_b queries
@@ -245,6 +247,28 @@ dsa_status_t dsa_forward(const dsa_forward_args_t *args, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
 dsa_status_t dsa_forward_workspace_size(const dsa_forward_args_t *args, size_t *bytes);
+
+/* ------------------------------------------------------------------------
+ * dsa_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc.  It allocates nothing.  The workspace
+ * dsa_forward would take lives in a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from
+ * the library's first use on that GPU to the end of the process.
+ *   args     as for dsa_forward (same validation, same results)
+ *   stream   the launch stream; the array of the stream's device is used
+ * Errors: DSA_ERR_WORKSPACE_TOO_SMALL, with nothing launched, when
+ * dsa_forward_workspace_size(args) exceeds DSA_NOALLOC_SCRATCH_BYTES (the
+ * decode workloads need 36 MiB at 32 x 32768 and 68 MiB at 64 histories of
+ * up to 131072 tokens; prefill needs far more unless the caller keeps scores
+ * and indices in its own buffers); otherwise as dsa_forward.
+ * All calls on one GPU share its array: calls on one GPU that may overlap in
+ * time (concurrent streams, or threads) race on it and must be serialised by
+ * the caller.  Consecutive calls on one stream are ordered and safe.
+ * ---------------------------------------------------------------------- */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+dsa_status_t dsa_forward_noalloc(const dsa_forward_args_t *args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decode-step cache append.  Writes the cache entries of `num_tokens` new

@@ -69,6 +69,7 @@ _SIGS = {
                                       ctypes.POINTER(c_size)],
     "dsa_forward": [ctypes.POINTER(dsa_forward_args_t), c_ptr, c_size, c_ptr],
     "dsa_forward_workspace_size": [ctypes.POINTER(dsa_forward_args_t), ctypes.POINTER(c_size)],
+    "dsa_forward_noalloc": [ctypes.POINTER(dsa_forward_args_t), c_ptr],
     "dsa_indexer_topk": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32, c_i32,
                          c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_f32, c_i32, c_ptr, c_ptr, c_size, c_ptr],
     "dsa_indexer_topk_workspace_size": [ctypes.POINTER(dsa_batch_t), ctypes.POINTER(dsa_kv_layout_t), c_i32, c_i32,
@@ -266,6 +267,13 @@ def dsa_forward(args, workspace=None, workspace_bytes=0, stream=None, check=True
                            _stream(stream))
     if check:
         _check(st, "dsa_forward")
+    return st
+
+
+def dsa_forward_noalloc(args, stream=None, check=True):
+    st = lib().dsa_forward_noalloc(ctypes.byref(args), _stream(stream))
+    if check:
+        _check(st, "dsa_forward_noalloc")
     return st
 
 

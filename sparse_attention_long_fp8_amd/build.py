@@ -26,7 +26,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 LIB_SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "module.hip", "validate.hip",
-               "libdsa.cpp", "module.cpp"]
+               "noalloc.hip", "libdsa.cpp", "module.cpp"]
 # the output projections are plain GEMMs, run by hipBLASLt, in a library of
 # their own (libdsa_proj.so) so that libdsa.so loads no GEMM library
 PROJ_SOURCES = ["projection.cpp"]

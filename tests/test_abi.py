@@ -21,7 +21,7 @@ def _layout(rows=8):
 def test_exports_match_header():
     lib = B.lib()
     names = B.header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
 
