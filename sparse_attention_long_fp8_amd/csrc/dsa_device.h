@@ -41,6 +41,25 @@ __device__ __forceinline__ int seq_of_row(const BatchDev &bt, int t) {
   return lo;
 }
 
+// The same sequence, found by a whole wave (every lane active) in a 64-ary
+// search: lane l reads entry b + l * step and a ballot of the entries <= t
+// picks the bracket, so up to 64 sequences cost one memory round trip (a
+// binary search pays one per halving).  Entries are non-decreasing; the
+// result is wave-uniform and in [0, num_seqs) for any array contents.
+__device__ __forceinline__ int seq_of_row_wave(const BatchDev &bt, int t) {
+  const int lane = __lane_id();
+  int b = 0;
+  for (int span = bt.num_seqs; span > 1;) {
+    const int step = (span + 63) >> 6;
+    const int pos = b + lane * step;
+    const bool le = pos < b + span && bt.q_seq_start[pos] <= t;
+    const int c = max((int)__popcll(__ballot(le)), 1);
+    b += (c - 1) * step;
+    span = min(step, span - (c - 1) * step);
+  }
+  return __builtin_amdgcn_readfirstlane(b);
+}
+
 // Query row t of sequence b sits at p = k_len[b] - nq_b + (t - q_seq_start[b])
 // and has n = p + 1 causal candidates (itself included).
 __device__ __forceinline__ int candidates_of_row(const BatchDev &bt, int b, int t) {

@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
   static_assert(kStagedPages <= kIdxThreads, "one thread per page base");
   __shared__ IdxStagedLds<KPB> sh;
   const int t = blockIdx.y;
-  const int b = __builtin_amdgcn_readfirstlane(seq_of_row(bt, t));
+  const int b = seq_of_row_wave(bt, t);
   const int n = __builtin_amdgcn_readfirstlane(candidates_of_row(bt, b, t));
   const int s_begin = blockIdx.x * KPB;
   if (s_begin >= n) return;

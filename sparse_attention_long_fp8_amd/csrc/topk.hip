@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
                                                          TopkSplit sp) {
   __shared__ TopkLds sh;
   const int t = blockIdx.x;
-  const int b = seq_of_row(bt, t);
+  const int b = seq_of_row_wave(bt, t);
   const int n_row = candidates_of_row(bt, b, t);
   int n = n_row;
   const float *row = scores + (int64_t)t * ld;

@@ -4,7 +4,9 @@ constant row (the whole row is one bin, past the candidate list), signed
 zeros, all-negative rows, rows longer than the LDS row cache, rows
 shorter than k, ReLU rows that are half exact zeros, k above 2048, ties
 spread over the parts of rows longer than 32768 (selected in two passes when
-the batch has few rows), and crafted rows of 16385 to 32768 scores in a
+the batch has few rows), decode-like rows of few-row batches at lengths
+around 8192, 12288 and 32768, rows where only every 32nd score is large, rows
+with -inf scores, heavy ties at the k-th score, and crafted rows of 16385 to 32768 scores in a
 small batch with k = 4096 and 4097 (ties across position 16384, ragged
 lengths).  Each row is its own sequence, so n_t = k_len[t]; entries
 past n_t are NaN and must never be read."""
@@ -47,6 +49,22 @@ def _rows(kind, rng):
                 np.concatenate([np.zeros(16384, np.float32), np.ones(8000, np.float32)])], 4096
     if kind == "mid_k_limit":
         return [np.full(30000, 0.5, np.float32), rng.integers(0, 4, 25000).astype(np.float32)], 4097
+    if kind == "decode_lengths":   # decode rows of few-row batches, around 4k-multiples
+        return [rng.standard_normal(n).astype(np.float32) for n in (8191, 8192, 8193, 12288, 12289, 32768,
+                                                                     32769, 131072)], 2048
+    if kind == "strided_high":   # every 32nd score is large, the rest small
+        n = 65536
+        r = rng.random(n).astype(np.float32)
+        r[(np.arange(2048, dtype=np.int64) * n) // 2048] += 10.0
+        return [r, rng.standard_normal(n).astype(np.float32)], 4000
+    if kind == "infinities":   # -inf scores, often and rarely
+        a = rng.standard_normal(40000).astype(np.float32)
+        a[::7] = -np.inf
+        b = rng.standard_normal(40000).astype(np.float32)
+        b[(np.arange(2048, dtype=np.int64) * 40000) // 2048 + 1] = -np.inf
+        return [a, b], 2048
+    if kind == "threshold_ties":   # the k-th score has hundreds of equal copies
+        return [rng.integers(0, 40, 32768).astype(np.float32), rng.integers(0, 200, 50000).astype(np.float32)], 2048
     if kind == "short_rows":
         return [rng.standard_normal(n).astype(np.float32) for n in (1, 10, 63, 64, 65)], 64
     raise KeyError(kind)
@@ -54,7 +72,8 @@ def _rows(kind, rng):
 
 @pytest.mark.parametrize("kind", ["ties_small_bins", "ties_few_values", "constant", "signed_zero",
                                   "all_negative", "long_rows", "short_rows", "relu_zeros", "k_above_staging",
-                                  "long_ties", "mid_ties", "mid_k_limit"])
+                                  "long_ties", "mid_ties", "mid_k_limit", "decode_lengths",
+                                  "strided_high", "infinities", "threshold_ties"])
 def test_topk_crafted_rows(kind, gpu):
     print("\n[topk-edge] %s" % kind, flush=True)
     rng = np.random.default_rng(zlib.crc32(kind.encode()))
