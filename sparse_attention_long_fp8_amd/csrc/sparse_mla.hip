@@ -11,6 +11,8 @@
 // The output stays in latent space (before W_UV).
 #include <hip/hip_bf16.h>
 
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -391,6 +393,19 @@ struct MlaLds {
   int32_t rows[kMaxSlots];  // resolved rows of the range (-1: masked slot)
 };
 
+// 128 heads: the P.V product is split over output columns (see the kernel),
+// which needs the P fragments, the rescale factors and the denominators in
+// LDS; three tile buffers leave the room.
+constexpr int kBufsSplit = 3;
+struct MlaLdsSplit {
+  uint8_t tile[kBufsSplit][kTileBytes];
+  int32_t rows[kMaxSlots];
+  v8bf p[8][64];        // P fragment of each wave's 16 heads, lane by lane
+  float alpha[128];     // rescale factor of each head (valid where resc is set)
+  int32_t resc[8];      // wave w rescaled its heads in this tile
+  float inv_l[128];     // 1 / denominator of each head
+};
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -406,7 +421,16 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   // waves below kTileLoads % NW issue one load more per tile than the others
   constexpr int kLHi = (kTileLoads + NW - 1) / NW;
   constexpr int kLLo = kTileLoads / NW;
-  __shared__ MlaLds sh;
+  // 128 heads: P.V split over output columns -- wave w accumulates every
+  // head's output over dims 64w .. 64w+63 -- so each V element is read from
+  // LDS by one wave instead of eight (transpose reads run at about 60% of the
+  // plain 16-byte read rate); the waves' P fragments go through LDS instead.
+  constexpr bool kSplit = NW == 8 && HT == 1;
+  constexpr int NB = kSplit ? kBufsSplit : kBufs;  // tile buffers
+  constexpr int kOt = kSplit ? kNt / NW : kNt;     // output dim tiles of a wave
+  constexpr int kOh = kSplit ? NW : HT;            // output head tiles of a wave
+  using Lds = typename std::conditional<kSplit, MlaLdsSplit, MlaLds>::type;
+  __shared__ Lds sh;
 
   const int t = blockIdx.x;
   const int split = blockIdx.y;
@@ -529,15 +553,19 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     }
   };
 
-  v4f o[HT][kNt];
+  // o[a][j]: heads 16a + 4g + i (i < 4) of the wave's head tile a (split:
+  // every wave's), dims 16 * (dim tile j) + n16 (split: dim tiles kOt*w + j)
+  v4f o[kOh][kOt];
   float m_ref[HT], l_part[HT];  // reference max (log2 domain), this lane's denominator share
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     m_ref[ht] = -INFINITY;
     l_part[ht] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kNt; ++i) o[ht][i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int a = 0; a < kOh; ++a)
+#pragma unroll
+    for (int i = 0; i < kOt; ++i) o[a][i] = v4f{0.f, 0.f, 0.f, 0.f};
   const float zscale = sm_scale * kLog2e;
 
   // The query loads must be complete (and known complete to the compiler)
@@ -546,12 +574,12 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   // together with tile 0's gather; the next tiles go out after.
   if (nblk > 0) gather(0, 0);
   wait_vmcnt<0>();
-  for (int p = 1; p < kBufs - 1 && p < nblk; ++p) gather(p, p);
+  for (int p = 1; p < NB - 1 && p < nblk; ++p) gather(p, p);
   lds_barrier();
 
   for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk % kBufs;
-    if (blk + kBufs - 1 < nblk) gather(blk + kBufs - 1, (blk + kBufs - 1) % kBufs);
+    const int buf = blk % NB;
+    if (blk + NB - 1 < nblk) gather(blk + NB - 1, (blk + NB - 1) % NB);
     const uint8_t *tile = sh.tile[buf];
     const int32_t *rows = sh.rows + blk * kBlk;
 
@@ -643,75 +671,134 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       }
       l_part[ht] = l_part[ht] * alpha[ht] + sum;
     }
-    if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        float r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = __shfl(alpha[ht], 4 * g + i, 64);
-#pragma unroll
-        for (int nt = 0; nt < kNt; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[ht][nt][i] *= r[i];
+    if constexpr (kSplit) {
+      // this wave's P fragment, rescale flag and factors go to LDS; after the
+      // barrier every wave reads all eight
+      *(v8bf *)&sh.p[wave][lane] = pf[0];
+      const bool any = __ballot(rescale) != 0;
+      if (lane == 0) sh.resc[wave] = any;
+      if (any) {  // (its address is computed here: a register held across the loop would spill)
+        const int ln = opaque_lane_id();
+        if (ln < 16) sh.alpha[16 * wave + ln] = alpha[0];
       }
-    }
+      lds_barrier();
+      // ---- O[all heads, dims 64w..64w+63] += P . V ----
+      // V fragments of the wave's four dim tiles (transpose reads, as below),
+      // then each head tile's P from LDS
+      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+      v8bf vb[kOt];
+#pragma unroll
+      for (int j = 0; j < kOt; ++j) {
+        const int nt = kOt * wave + j;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
+        __builtin_memcpy(&vb[j], &lo, 8);
+        __builtin_memcpy((char *)&vb[j] + 8, &hi, 8);
+      }
+      const v4i rf0 = *(const v4i *)&sh.resc[0], rf1 = *(const v4i *)&sh.resc[4];
+#pragma unroll
+      for (int a = 0; a < kOh; ++a) {
+        const v8bf pa = sh.p[a][lane];
+        if ((a < 4 ? rf0[a & 3] : rf1[a & 3]) != 0) {  // wave-uniform, rare
+          float r[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = sh.alpha[16 * a + 4 * g + i];
+#pragma unroll
+          for (int j = 0; j < kOt; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[a][j][i] *= r[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kOt; ++j) o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[j], o[a][j], 0, 0, 0);
+      }
+    } else {
+      if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
+  #pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          float r[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = __shfl(alpha[ht], 4 * g + i, 64);
+  #pragma unroll
+          for (int nt = 0; nt < kNt; ++nt)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) o[ht][nt][i] *= r[i];
+        }
+      }
 
-    // ---- O += P . V ----
-    // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
-    // of a 16-dim tile); the transpose read hands lane i column i of the four
-    // rows: 4 consecutive tokens of one dim, the B-operand slot order
-    const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
-#pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
-      v8bf vb;
-      __builtin_memcpy(&vb, &lo, 8);
-      __builtin_memcpy((char *)&vb + 8, &hi, 8);
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
+      // ---- O += P . V ----
+      // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
+      // of a 16-dim tile); the transpose read hands lane i column i of the four
+      // rows: 4 consecutive tokens of one dim, the B-operand slot order
+      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+  #pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
+        v8bf vb;
+        __builtin_memcpy(&vb, &lo, 8);
+        __builtin_memcpy((char *)&vb + 8, &hi, 8);
+  #pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vb, o[ht][nt], 0, 0, 0);
+      }
+      // keep three V fragments (6 transpose reads) ahead of the PV MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_PV_AHEAD, 0);
+  #pragma unroll
+      for (int i = 0; i < kNt - DSA_PV_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, HT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, DSA_PV_AHEAD * HT, 0);
     }
-    // keep three V fragments (6 transpose reads) ahead of the PV MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_PV_AHEAD, 0);
-#pragma unroll
-    for (int i = 0; i < kNt - DSA_PV_AHEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, HT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, DSA_PV_AHEAD * HT, 0);
 
     // the next tile must have landed; the ones after it may stay in flight
-    wait_tiles(min(nblk - 1, blk + kBufs - 1) - (blk + 1));
+    wait_tiles(min(nblk - 1, blk + NB - 1) - (blk + 1));
     lds_barrier();
   }
 
   // ---- finish: denominators, output ----
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    float lt = l_part[ht];
+  __hip_bfloat16 *ot = nsplit == 1 ? out + (int64_t)t * H * kDv : part_o + ((int64_t)t * nsplit + split) * H * kDv;
+  float *lt_dst = nsplit == 1 ? lse : part_lse + ((int64_t)t * nsplit + split) * H - (int64_t)t * H;
+  if constexpr (kSplit) {
+    // the wave's heads' 1 / l and lse; then every head's row of the wave's dims
+    float lt = l_part[0];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    // lane n16 holds (m, l) of head HW*w + 16*ht + n16
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_h = lt > 0.f ? (m_ref[ht] + log2f(lt)) * kLn2 : -INFINITY;
-    float ir[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ir[i] = __shfl(inv, 4 * g + i, 64);
-    const int h0 = HW * wave + 16 * ht + 4 * g;  // first head of this lane's O rows
-    __hip_bfloat16 *ot = nsplit == 1 ? out + (int64_t)t * H * kDv
-                                     : part_o + ((int64_t)t * nsplit + split) * H * kDv;
-#pragma unroll
-    for (int nt = 0; nt < kNt; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ot[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = __float2bfloat16(o[ht][nt][i] * ir[i]);
     if (g == 0) {
-      if (nsplit == 1) {
-        if (lse) lse[(int64_t)t * H + HW * wave + 16 * ht + n16] = lse_h;
-      } else {
-        part_lse[((int64_t)t * nsplit + split) * H + HW * wave + 16 * ht + n16] = lse_h;
-      }
+      sh.inv_l[16 * wave + n16] = lt > 0.f ? 1.f / lt : 0.f;
+      if (lt_dst) lt_dst[(int64_t)t * H + 16 * wave + n16] = lt > 0.f ? (m_ref[0] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int a = 0; a < kOh; ++a) {
+      float ir[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ir[i] = sh.inv_l[16 * a + 4 * g + i];
+#pragma unroll
+      for (int j = 0; j < kOt; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ot[(int64_t)(16 * a + 4 * g + i) * kDv + 16 * (kOt * wave + j) + n16] = __float2bfloat16(o[a][j][i] * ir[i]);
+    }
+  } else {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float lt = l_part[ht];
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      // lane n16 holds (m, l) of head HW*w + 16*ht + n16
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse_h = lt > 0.f ? (m_ref[ht] + log2f(lt)) * kLn2 : -INFINITY;
+      float ir[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ir[i] = __shfl(inv, 4 * g + i, 64);
+      const int h0 = HW * wave + 16 * ht + 4 * g;  // first head of this lane's O rows
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ot[(int64_t)(h0 + i) * kDv + 16 * nt + n16] = __float2bfloat16(o[ht][nt][i] * ir[i]);
+      if (g == 0 && lt_dst) lt_dst[(int64_t)t * H + HW * wave + 16 * ht + n16] = lse_h;
     }
   }
 }
