@@ -340,26 +340,31 @@ __global__ __launch_bounds__(256) void mla_f32_combine_kernel(int heads, int d_v
 //   * rows: every slot of the range is resolved once (index -> page -> row)
 //     into LDS before the tile loop, so the loop issues no dependent loads;
 //   * gather: the 32 selected 1152-byte key rows of a tile go straight into
-//     LDS with 16-byte global->LDS loads (a 1184-byte row pitch spreads the
-//     LDS banks; it measured fastest of the pitches from 1168 to 1280 bytes).
-//     A tile is exactly 37 wave-wide 1 KB loads.  Four tile buffers keep
-//     three tiles in flight while one is computed; a wave issues the same
-//     number of loads for every tile, so a per-wave vmcnt wait retires
-//     exactly the tile that is needed next;
+//     LDS with 16-byte global->LDS loads: each row's 1024-byte latent part at
+//     a 1040-byte pitch (one wave-wide load from a scalar base address), the
+//     32 128-byte rotary parts after them, their 16-byte chunks XOR-permuted
+//     by the row (8 rows a load).  A tile is exactly 36 wave-wide loads, spread
+//     over the waves with the same count for every tile, so a per-wave vmcnt
+//     wait retires exactly the tile that is needed next; three (128 heads) or
+//     four tile buffers keep the next tiles in flight while one is computed;
 //   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
 //       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
 //       registers for the whole launch; each LDS fragment feeds every head
-//       tile of the wave);
+//       tile of the wave).  A-operand row m of each 16-token half is token
+//       tok_of(m) (a fixed permutation, below), so that the value reads of
+//       the PV product, which follow the accumulator's token order, meet
+//       distinct LDS banks at the 1040-byte pitch;
 //   * online softmax per head in the exp2 domain.  A head's reference max
 //     only moves when a tile's max exceeds it by more than 8 (so the
 //     unnormalised terms stay below 2^8); only then are its O rows and
 //     denominator rescaled, which keeps the rescale out of the steady state;
 //   * O[16 heads x 512] += P[16 x 32] . V[32 x 512] per head tile.  The S^T
-//     accumulator of lane (g, head) holds tokens 4g+i of each 16-token half,
-//     which is the A-operand slot set of the PV product once its K order is
-//     permuted to match (tokens 4g..4g+3 and 16+4g..16+4g+3 for lane group
-//     g); V is read with the same permutation by LDS transpose reads, so P
-//     never leaves its registers.
+//     accumulator of lane (g, head) holds register i = tokens tok_of(4g+i) of
+//     each 16-token half, which is the A-operand slot set of the PV product
+//     once its K order is permuted to match; V is read in the same order by
+//     LDS transpose reads, so P needs no reordering (with 8 waves of 128 heads
+//     the PV product is split over output columns instead: every wave's P
+//     fragments pass through LDS, in the same lane order).
 // With more than one slot range per row (decode: few rows), each range
 // writes its normalised output in bf16 plus its lse, merged by mla_combine.
 // --------------------------------------------------------------------------
@@ -375,6 +380,12 @@ constexpr int kLatBytes = kDv * 2;             // 1024: one wave-wide 16-byte lo
 constexpr int kLatStride = kLatBytes + 16;     // LDS pitch of the latent parts
 constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128
 constexpr int kRopeOff = kBlk * kLatStride;    // rotary parts follow the latent parts
+// Token of A-operand row m (0..15) of a 16-token half of the QK product.  Lane
+// group g of a PV value read then addresses tokens 4r + (g with its two bits
+// swapped), r = 0..3: in each half-wave the eight rows sit 8 banks apart at the
+// 1040-byte pitch (4 banks a row), so the 32 lanes' 8-byte reads of 4 chunks a
+// row cover the 64 banks once.
+__device__ __forceinline__ int tok_of(int m) { return 4 * (m & 3) + (((m >> 1) & 2) | ((m >> 3) & 1)); }
 constexpr int kTileBytes = kRopeOff + kBlk * kRopeBytes;
 constexpr int kRopeLoads = kBlk * kRopeBytes / 1024;  // 4: eight rows' rotary parts each
 constexpr int kTileLoads = kBlk + kRopeLoads;  // 36 wave-wide 1 KB loads per tile
@@ -592,11 +603,12 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     }
     // A fragments: K-steps 0-15 from the latent parts, 16-17 from the
     // rotary parts (chunk c of row r at position c ^ (r % 8))
-    const uint8_t *alat = tile + n16 * kLatStride + 16 * g;
-    const uint8_t *arope = tile + kRopeOff + n16 * kRopeBytes;
+    const int ar = tok_of(n16);  // A-operand row n16 is this token of each half
+    const uint8_t *alat = tile + ar * kLatStride + 16 * g;
+    const uint8_t *arope = tile + kRopeOff + ar * kRopeBytes;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      const int ro = 16 * ((4 * (ks - kKsLat) + g) ^ (n16 & 7));
+      const int ro = 16 * ((4 * (ks - kKsLat) + g) ^ (ar & 7));
       const v8bf a0 = ks < kKsLat ? *(const v8bf *)(alat + 64 * ks) : *(const v8bf *)(arope + ro);
       const v8bf a1 = ks < kKsLat ? *(const v8bf *)(alat + 16 * kLatStride + 64 * ks)
                                   : *(const v8bf *)(arope + 16 * kRopeBytes + ro);
@@ -615,12 +627,12 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * DSA_QK_AHEAD * HT, 1);
 
-    // ---- online softmax (this lane: head n16 of each tile; tokens 4g+i, 16+4g+i) ----
+    // ---- online softmax (this lane: head n16 of each tile; tokens tok_of(4g+i), 16+tok_of(4g+i)) ----
     bool ok[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ok[i] = rows[4 * g + i] >= 0;
-      ok[4 + i] = rows[16 + 4 * g + i] >= 0;
+      ok[i] = rows[tok_of(4 * g + i)] >= 0;
+      ok[4 + i] = rows[16 + tok_of(4 * g + i)] >= 0;
     }
     v8bf pf[HT];
     float alpha[HT];
@@ -685,7 +697,7 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       // ---- O[all heads, dims 64w..64w+63] += P . V ----
       // V fragments of the wave's four dim tiles (transpose reads, as below),
       // then each head tile's P from LDS
-      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+      const uint8_t *vrow = tile + tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
       v8bf vb[kOt];
 #pragma unroll
       for (int j = 0; j < kOt; ++j) {
@@ -695,22 +707,39 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
         __builtin_memcpy(&vb[j], &lo, 8);
         __builtin_memcpy((char *)&vb[j] + 8, &hi, 8);
       }
+      // rescales first, behind one wave-uniform branch (rare), so that the
+      // products below are one block in which P reads run ahead of the MFMAs
       const v4i rf0 = *(const v4i *)&sh.resc[0], rf1 = *(const v4i *)&sh.resc[4];
+      if ((rf0.x | rf0.y | rf0.z | rf0.w | rf1.x | rf1.y | rf1.z | rf1.w) != 0) {
+#pragma unroll
+        for (int a = 0; a < kOh; ++a) {
+          if ((a < 4 ? rf0[a & 3] : rf1[a & 3]) != 0) {
+            float r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = sh.alpha[16 * a + 4 * g + i];
+#pragma unroll
+            for (int j = 0; j < kOt; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[a][j][i] *= r[i];
+          }
+        }
+      }
+      v8bf pa = sh.p[0][lane];
 #pragma unroll
       for (int a = 0; a < kOh; ++a) {
-        const v8bf pa = sh.p[a][lane];
-        if ((a < 4 ? rf0[a & 3] : rf1[a & 3]) != 0) {  // wave-uniform, rare
-          float r[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = sh.alpha[16 * a + 4 * g + i];
-#pragma unroll
-          for (int j = 0; j < kOt; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[a][j][i] *= r[i];
-        }
+        v8bf pn;
+        if (a + 1 < kOh) pn = sh.p[a + 1][lane];  // one head tile ahead
 #pragma unroll
         for (int j = 0; j < kOt; ++j) o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[j], o[a][j], 0, 0, 0);
+        if (a + 1 < kOh) pa = pn;
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+#pragma unroll
+      for (int a = 0; a + 2 < kOh; ++a) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kOt, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kOt, 3);
     } else {
       if (__ballot(rescale)) {  // O rows of this lane are heads 4g+i of each tile
   #pragma unroll
@@ -729,7 +758,7 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
       // of a 16-dim tile); the transpose read hands lane i column i of the four
       // rows: 4 consecutive tokens of one dim, the B-operand slot order
-      const uint8_t *vrow = tile + (4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+      const uint8_t *vrow = tile + tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
   #pragma unroll
       for (int nt = 0; nt < kNt; ++nt) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
