@@ -35,8 +35,11 @@ PROJ_LINK = ["-L" + PKG, "-ldsa", "-Wl,-rpath,$ORIGIN", "-L/opt/rocm/lib", "-lhi
 # Per-source flags.  The FP8 indexer reads every MFMA result with VALU code
 # (ReLU, head weights); keeping the accumulators in ordinary VGPRs saves one
 # AGPR->VGPR move per element.
-SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
-PROBE_SOURCES = ["probe.hip"]
+# The rate probes keep their accumulators in VGPRs too: with AGPR accumulators
+# the compiler rotates them through v_accvgpr moves inside the timed loops.
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "rates.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+PROBE_SOURCES = ["probe.hip", "rates.hip"]
 
 LIB_PATH = os.path.join(PKG, "libdsa.so")
 PROJ_PATH = os.path.join(PKG, "libdsa_proj.so")
