@@ -22,7 +22,8 @@ FULL = ["decode_32k", "prefill_16k", "prefill_64k", "paged_decode"]
 def _sample(wl, rows):
     """Every row of the decode workloads; on the prefills the rows at the ends
     and around the k boundary plus seeded rows in equal strata (the 64k
-    prefill: the benchmark's 256-row oracle sample)."""
+    prefill: 256 rows drawn like the benchmark's oracle sample, with another
+    seed)."""
     T = len(rows)
     if wl.kind == "decode":
         return list(range(T))
