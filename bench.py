@@ -123,8 +123,10 @@ def kernel_name(stage, wl, lay):
 def fused_applies(wl, lay):
     """Whether dsa_forward without kept scores takes the fused indexer ->
     top-k kernel (the launcher's choice): FP8, 64 x 128 indexer heads,
-    contiguous keys, at least 8 query rows per sequence."""
-    return wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and not wl.paged and lay.max_q_per_seq >= 8
+    contiguous keys or paged histories of at most 131072 keys, at least 8
+    query rows per sequence."""
+    return (wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and lay.max_q_per_seq >= 8
+            and (not wl.paged or lay.max_k_len <= 131072))
 
 
 def source_hash(stage):

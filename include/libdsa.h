@@ -157,7 +157,9 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
  * ascending position and keeps a bounded list of candidates above a running
  * threshold, selecting from it exactly (same ties, same order, -1 padding).
  * It applies to FP8 keys with h_i == 64 and d_i == 128 in a contiguous
- * cache, for batches with max_q_per_seq >= 8 (prefill, chunked prefill);
+ * cache, or in a paged one when max_k_len <= 131072 (each workgroup keeps
+ * the page numbers of its sequence's history in LDS), for batches with
+ * max_q_per_seq >= 8 (prefill, chunked prefill);
  * its workspace holds (2k + 128, rounded up to 64) candidates of 8 bytes per
  * query row.  Other shapes run the two stages with the fp32 score rows in
  * the workspace, followed by dsa_topk's own workspace when it needs one.

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
 }
 
 // --------------------------------------------------------------------------
-// Fused indexer -> top-k (prefill, contiguous keys).
+// Fused indexer -> top-k (prefill; contiguous keys, or paged histories of up
+// to kFusedMaxPages pages).
 //
 // The top-k of a row is the top-k of the union of any partition of its keys,
 // because every score depends on one key only ("DeepSeek Sparse Attention DSA
@@ -346,10 +347,17 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
 // the entries above tau and those first equal ones, with ballot prefix counts
 // for the write positions.
 // --------------------------------------------------------------------------
+// Paged keys: the page of every 64 keys a workgroup streams, resolved into
+// LDS before the loop (4 bytes a page), so histories of up to
+// fused_topk_max_paged_keys keys.
+constexpr int kFusedMaxPages = fused_topk_max_paged_keys / kPageSize;
+
+template <bool PAGED>
 struct IdxFusedLds {
   uint8_t keys[kTBufs][kTStageBytes];
   float ksc[kTBufs][kTStageKeys];
   uint32_t hist[4][256];  // one radix histogram per wave
+  int32_t page[PAGED ? kFusedMaxPages : 1];
 };
 
 // Exclusive prefix over the wave's lanes, and wave total, of c in [0, 7].
@@ -435,16 +443,16 @@ __device__ void wave_select_kth(const float *cs, int n, int k, uint32_t *hist, u
   need_eq = need;
 }
 
-template <int MT, int QW>
+template <int MT, int QW, bool PAGED>
 __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
-    BatchDev bt, const int64_t *__restrict__ k_seq_start, const uint8_t *__restrict__ q,
+    BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q,
     const float *__restrict__ q_scale, const float *__restrict__ w, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, float scale, int topk, int cap, float *__restrict__ cand_s,
     int32_t *__restrict__ cand_i, int32_t *__restrict__ indices) {
   constexpr int H = 32 * MT;
   constexpr int QT = 4 * QW;
   constexpr int kSub = kTStageKeys / 32;
-  __shared__ IdxFusedLds sh;
+  __shared__ IdxFusedLds<PAGED> sh;
 
   const int b = blockIdx.y;
   const int q0 = bt.q_seq_start[b];
@@ -456,7 +464,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
   const int first_pos = kl - nq;
   const int n_max = first_pos + min(nq, g0 + QT);
   const int nst = (n_max + kTStageKeys - 1) / kTStageKeys;
-  const int64_t kbase = k_seq_start[b];
+  const int64_t kbase = PAGED ? 0 : kd.k_seq_start[b];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -494,10 +502,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       }
     row_scale[j] = q_scale[t] * scale;
   }
+  if constexpr (PAGED) {  // the launcher admits only histories of at most kFusedMaxPages pages
+    const int npages = min((n_max + kPageSize - 1) >> kPageShift, kFusedMaxPages);
+    for (int p = tid; p < npages; p += kIdxThreads) sh.page[p] = kd.page_table[(int64_t)b * kd.stride + p];
+  }
   // (the barrier alone does not wait for global loads)
   wait_vmcnt<0>();
   __syncthreads();
 
+  // flat row of key s of the sequence
+  auto row_of = [&](int s) __attribute__((always_inline)) -> int64_t {
+    if constexpr (PAGED) return ((int64_t)sh.page[s >> kPageShift] << kPageShift) + (s & (kPageSize - 1));
+    else return kbase + s;
+  };
   const uint32_t keys0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.keys[0][0]));
   const uint32_t ksc0 = __builtin_amdgcn_readfirstlane(lds_addr(&sh.ksc[0][0]));
   auto stage = [&](int si) __attribute__((always_inline)) {
@@ -507,11 +524,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
     for (int m = 0; m < kTStageLoads / 4; ++m) {
       const int j = wave + 4 * m;
       const int r = 8 * j + (lane >> 3);
-      const int64_t row = kbase + min(s_stage + r, n_max - 1);
+      const int64_t row = row_of(min(s_stage + r, n_max - 1));
       lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kTStageBytes + 1024 * j);
     }
     if (wave < 2) {
-      const int64_t row = kbase + min(s_stage + 64 * wave + lane, n_max - 1);
+      const int64_t row = row_of(min(s_stage + 64 * wave + lane, n_max - 1));
       lds_dma4_at(k_scale + row, ksc0 + buf * (kTStageKeys * 4) + 256 * wave);
     }
   };
@@ -839,20 +856,24 @@ size_t fused_topk_workspace_bytes(int num_queries, int k) {
   return 2 * one;
 }
 
-hipError_t launch_indexer_topk_fused(const BatchDev &bt, const int64_t *k_seq_start, int num_seqs,
-                                     int num_queries, int max_q_per_seq, const uint8_t *q,
-                                     const float *q_scale, const float *w, const uint8_t *k,
-                                     const float *k_scale, float scale, int topk, int32_t *indices,
-                                     void *workspace, hipStream_t stream) {
+hipError_t launch_indexer_topk_fused(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
+                                     int max_q_per_seq, int max_k_len, const uint8_t *q, const float *q_scale,
+                                     const float *w, const uint8_t *k, const float *k_scale, float scale, int topk,
+                                     int32_t *indices, void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
+  if (kd.paged && max_k_len > kFusedMaxPages * kPageSize) return hipErrorInvalidValue;
   constexpr int QW = 2;
   const int cap = fused_topk_cap(topk);
   const size_t one = ((size_t)num_queries * cap * 4 + 255) / 256 * 256;
   float *cand_s = (float *)workspace;
   int32_t *cand_i = (int32_t *)((char *)workspace + one);
   const dim3 grid((max_q_per_seq + 4 * QW - 1) / (4 * QW), num_seqs);
-  hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, k_seq_start, q,
-                     q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
+  if (kd.paged)
+    hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW, true>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                       q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
+  else
+    hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW, false>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
+                       q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
   return hipGetLastError();
 }
 

@@ -125,6 +125,35 @@ def test_workspace_sizes_and_too_small():
     assert B.dsa_forward(args, 0x100010, need, check=False) == B.DSA_ERR_INVALID_ARGUMENT  # misaligned
 
 
+def test_fused_indexer_topk_workspace_choice():
+    """dsa_indexer_topk takes the fused kernel (candidate lists, 8 bytes per
+    entry, 2k + 128 entries rounded to 64 per row) for prefill batches with
+    contiguous keys or paged histories up to 131072 keys; past that, and for
+    decode batches, the two stages (fp32 score rows, then top-k's own)."""
+    k = 2048
+    cap = (2 * k + 128 + 63) // 64 * 64
+
+    def r256(x):
+        return -(-x // 256) * 256
+
+    def ws(T, maxq, maxk, paged):
+        bt = B.dsa_batch_t(T // maxq, T, 0x1000, 0x2000, maxq, maxk)
+        ly = (B.dsa_kv_layout_t(1, None, 0x5000, -(-maxk // 64), 64, 1 << 22) if paged
+              else B.dsa_kv_layout_t(0, 0x3000, None, 0, 64, 1 << 22))
+        return B.dsa_indexer_topk_workspace_size(bt, ly, B.DSA_FP8_E4M3, 64, 128, k)
+
+    def unfused(T, maxq, maxk):
+        return r256(T * (-(-maxk // 4) * 4) * 4) + B.dsa_topk_workspace_size(
+            B.dsa_batch_t(T // maxq, T, 0x1000, 0x2000, maxq, maxk), k)
+
+    fused = 2 * r256(4096 * cap * 4)
+    assert ws(4096, 4096, 131072, False) == fused
+    assert ws(4096, 4096, 131072, True) == fused
+    assert ws(4096, 4096, 131073, True) == unfused(4096, 4096, 131073)
+    assert ws(4096, 4096, 140000, False) == fused            # contiguous keys: no length limit
+    assert ws(32, 1, 32768, False) == unfused(32, 1, 32768)   # decode rows: the two stages
+
+
 def test_empty_batch_launches_nothing():
     empty = B.dsa_batch_t(1, 0, None, None, 0, 0)
     ly = _layout(1)

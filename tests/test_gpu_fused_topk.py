@@ -4,8 +4,9 @@ dsa_topk) on the same inputs -- the fused kernel computes the same scores
 and selects from bounded candidate lists -- and, end to end, agree with the
 oracle's selection on the oracle's scores up to near-ties of the k-th score.
 Cases: a causal prefill with several compactions of every long row's list
-(k = 512 and k = 64), ragged chunked prefill over three sequences, and rows
-made all ties (zero head weights), where the k lowest positions must win."""
+(k = 512 and k = 64), ragged chunked prefill over three sequences, the same
+two shapes over a paged cache (pages scattered over the pool), and rows made
+all ties (zero head weights), where the k lowest positions must win."""
 
 import numpy as np
 import pytest
@@ -23,6 +24,10 @@ CASES = {
     "prefill_1500_k64": synth.Workload("fused_prefill_k64", 33, "prefill", 1, 1500, top_k=64, heads=16),
     "chunk_3seq_k256": synth.Workload("fused_chunk", 32, "chunk", 3, 0, ctx_range=(900, 2500), q_per_seq=40,
                                       top_k=256, heads=16),
+    "prefill_paged_2500_k128": synth.Workload("fused_prefill_paged", 34, "prefill", 1, 2500, top_k=128, heads=16,
+                                              paged=True),
+    "chunk_paged_3seq_k256": synth.Workload("fused_chunk_paged", 35, "chunk", 3, 0, ctx_range=(900, 2500),
+                                            q_per_seq=40, top_k=256, heads=16, paged=True),
 }
 
 
@@ -46,7 +51,7 @@ def case(request, gpu):
 
 def test_fused_equals_separate_stages(case):
     k = case.wl.top_k
-    assert case.lay.max_q_per_seq >= 8 and not case.paged  # the fused kernel applies
+    assert case.lay.max_q_per_seq >= 8 and case.lay.max_k_len <= 131072  # the fused kernel applies
     got = _fused(case, k).cpu().numpy()
     want = case.topk(case.indexer(), k=k).cpu().numpy()
     bad = np.nonzero((got != want).any(axis=1))[0]
