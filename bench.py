@@ -107,7 +107,7 @@ def kernel_name(stage, wl, lay):
     if stage == "indexer":
         if not wl.fp8:
             return "indexer_f32_kernel"
-        return "indexer_fp8_tiled_kernel" if lay.max_q_per_seq >= 8 and wl.h_i == 64 else "indexer_fp8_staged_kernel"
+        return "indexer_fp8_tiled_kernel" if lay.max_q_per_seq >= 8 else "indexer_fp8_staged_kernel"
     if stage == "topk":
         return "topk_kernel"
     if not wl.fp8:
@@ -122,10 +122,10 @@ def kernel_name(stage, wl, lay):
 
 def fused_applies(wl, lay):
     """Whether dsa_forward without kept scores takes the fused indexer ->
-    top-k kernel (the launcher's choice): FP8, 64 x 128 indexer heads,
-    contiguous keys or paged histories of at most 131072 keys, at least 8
-    query rows per sequence."""
-    return (wl.fp8 and wl.h_i == 64 and wl.d_i == 128 and lay.max_q_per_seq >= 8
+    top-k kernel (the launcher's choice): FP8, 32, 64 or 128 x 128 indexer
+    heads, contiguous keys or paged histories of at most 131072 keys, at
+    least 8 query rows per sequence."""
+    return (wl.fp8 and wl.h_i in (32, 64, 128) and wl.d_i == 128 and lay.max_q_per_seq >= 8
             and (not wl.paged or lay.max_k_len <= 131072))
 
 

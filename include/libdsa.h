@@ -156,7 +156,7 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
  * only ([G] Stage 1, item 3); the fused kernel streams each row's keys in
  * ascending position and keeps a bounded list of candidates above a running
  * threshold, selecting from it exactly (same ties, same order, -1 padding).
- * It applies to FP8 keys with h_i == 64 and d_i == 128 in a contiguous
+ * It applies to FP8 keys with h_i of 32, 64 or 128 and d_i == 128 in a contiguous
  * cache, or in a paged one when max_k_len <= 131072 (each workgroup keeps
  * the page numbers of its sequence's history in LDS), for batches with
  * max_q_per_seq >= 8 (prefill, chunked prefill);

@@ -22,16 +22,16 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
                               const float *k_scale, float scale, float *scores, int64_t ld,
                               hipStream_t stream);
 
-// Fused indexer -> top-k (FP8, 64 heads x 128; contiguous keys, or paged
+// Fused indexer -> top-k (FP8, 32, 64 or 128 heads x 128; contiguous keys, or paged
 // histories of at most fused_topk_max_paged_keys keys): candidate list
 // capacity per row and workspace bytes.
 int fused_topk_cap(int k);
 size_t fused_topk_workspace_bytes(int num_queries, int k);
 constexpr int fused_topk_max_paged_keys = 2048 * 64;
 hipError_t launch_indexer_topk_fused(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
-                                     int max_q_per_seq, int max_k_len, const uint8_t *q, const float *q_scale,
-                                     const float *w, const uint8_t *k, const float *k_scale, float scale, int topk,
-                                     int32_t *indices, void *workspace, hipStream_t stream);
+                                     int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,
+                                     const float *q_scale, const float *w, const uint8_t *k, const float *k_scale,
+                                     float scale, int topk, int32_t *indices, void *workspace, hipStream_t stream);
 
 // Top-k; batches of few rows with histories past the LDS row cache use a
 // workspace of topk_workspace_bytes (0 otherwise).

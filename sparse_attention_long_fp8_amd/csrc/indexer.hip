@@ -857,23 +857,34 @@ size_t fused_topk_workspace_bytes(int num_queries, int k) {
 }
 
 hipError_t launch_indexer_topk_fused(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
-                                     int max_q_per_seq, int max_k_len, const uint8_t *q, const float *q_scale,
-                                     const float *w, const uint8_t *k, const float *k_scale, float scale, int topk,
-                                     int32_t *indices, void *workspace, hipStream_t stream) {
+                                     int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,
+                                     const float *q_scale, const float *w, const uint8_t *k, const float *k_scale,
+                                     float scale, int topk, int32_t *indices, void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
   if (kd.paged && max_k_len > kFusedMaxPages * kPageSize) return hipErrorInvalidValue;
-  constexpr int QW = 2;
   const int cap = fused_topk_cap(topk);
   const size_t one = ((size_t)num_queries * cap * 4 + 255) / 256 * 256;
   float *cand_s = (float *)workspace;
   int32_t *cand_i = (int32_t *)((char *)workspace + one);
-  const dim3 grid((max_q_per_seq + 4 * QW - 1) / (4 * QW), num_seqs);
-  if (kd.paged)
-    hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW, true>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                       q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
-  else
-    hipLaunchKernelGGL((indexer_topk_fused_kernel<2, QW, false>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                       q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);
+  // two rows a wave, one at 128 heads (whose query block and weights fill the registers)
+  const int qw = h_i == 128 ? 1 : 2;
+  const dim3 grid((max_q_per_seq + 4 * qw - 1) / (4 * qw), num_seqs);
+#define DSA_FUSED(MT, QW)                                                                                       \
+  do {                                                                                                          \
+    if (kd.paged)                                                                                               \
+      hipLaunchKernelGGL((indexer_topk_fused_kernel<MT, QW, true>), grid, dim3(kIdxThreads), 0, stream, bt, kd, \
+                         q, q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);                 \
+    else                                                                                                        \
+      hipLaunchKernelGGL((indexer_topk_fused_kernel<MT, QW, false>), grid, dim3(kIdxThreads), 0, stream, bt,    \
+                         kd, q, q_scale, w, k, k_scale, scale, topk, cap, cand_s, cand_i, indices);             \
+  } while (0)
+  switch (h_i) {
+    case 32: DSA_FUSED(1, 2); break;
+    case 64: DSA_FUSED(2, 2); break;
+    case 128: DSA_FUSED(4, 1); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DSA_FUSED
   return hipGetLastError();
 }
 
@@ -882,12 +893,21 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
                               const float *q_scale, const float *w, const uint8_t *k,
                               const float *k_scale, float scale, float *scores, int64_t ld,
                               hipStream_t stream) {
-  if (max_q_per_seq >= 8 && h_i == 64) {
-    constexpr int QW = 2;
-    dim3 grid((max_k_len + kTKeysPerBlock - 1) / kTKeysPerBlock, (max_q_per_seq + 4 * QW - 1) / (4 * QW),
-              num_seqs);
-    hipLaunchKernelGGL((indexer_fp8_tiled_kernel<2, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q,
-                       q_scale, w, k, k_scale, scale, scores, ld);
+  if (max_q_per_seq >= 8) {
+    // two rows a wave, one at 128 heads (whose query block and weights fill the registers)
+    const int qw = h_i == 128 ? 1 : 2;
+    const dim3 grid((max_k_len + kTKeysPerBlock - 1) / kTKeysPerBlock, (max_q_per_seq + 4 * qw - 1) / (4 * qw),
+                    num_seqs);
+#define DSA_TILED(MT, QW)                                                                                    \
+  hipLaunchKernelGGL((indexer_fp8_tiled_kernel<MT, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q, \
+                     q_scale, w, k, k_scale, scale, scores, ld)
+    switch (h_i) {
+      case 32: DSA_TILED(1, 2); break;
+      case 64: DSA_TILED(2, 2); break;
+      case 128: DSA_TILED(4, 1); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef DSA_TILED
     return hipGetLastError();
   }
   const bool one_round = (int64_t)((max_k_len + 2047) / 2048) * num_queries <= staged_resident(h_i);

@@ -149,12 +149,12 @@ size_t mla_ws(const dsa_batch_t *bt, dsa_dtype_t dt, int32_t heads, int32_t d_v,
   return dsa::mla_bf16_workspace_bytes(bt->num_queries, heads, d_v, k);
 }
 
-// The fused indexer -> top-k kernel covers FP8 keys of 64 heads x 128 in a
-// contiguous cache, or a paged one with histories of at most
+// The fused indexer -> top-k kernel covers FP8 keys of 32, 64 or 128 heads x
+// 128 in a contiguous cache, or a paged one with histories of at most
 // fused_topk_max_paged_keys keys, for batches with at least 8 query rows per
 // sequence.
 bool fused_applies(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i, int32_t d_i) {
-  return dt == DSA_FP8_E4M3 && h_i == 64 && d_i == 128 && bt->max_q_per_seq >= 8 &&
+  return dt == DSA_FP8_E4M3 && (h_i == 32 || h_i == 64 || h_i == 128) && d_i == 128 && bt->max_q_per_seq >= 8 &&
          (!ly->paged || bt->max_k_len <= dsa::fused_topk_max_paged_keys);
 }
 
@@ -425,7 +425,7 @@ dsa_status_t dsa_indexer_topk(const dsa_batch_t *batch, const dsa_kv_layout_t *k
   if (fused_applies(batch, keys, dtype, h_i, d_i))
     return hip_status(dsa::launch_indexer_topk_fused(to_dev(batch), to_dev(keys), batch->num_seqs,
                                                       batch->num_queries, batch->max_q_per_seq, batch->max_k_len,
-                                                      (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx,
+                                                      h_i, (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx,
                                                       k_scale, scale, k, indices, workspace, stream),
                       "fused indexer + top-k launch");
   const int64_t ld = (int64_t)round_up((size_t)batch->max_k_len, 4);

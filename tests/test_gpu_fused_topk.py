@@ -5,8 +5,9 @@ and selects from bounded candidate lists -- and, end to end, agree with the
 oracle's selection on the oracle's scores up to near-ties of the k-th score.
 Cases: a causal prefill with several compactions of every long row's list
 (k = 512 and k = 64), ragged chunked prefill over three sequences, the same
-two shapes over a paged cache (pages scattered over the pool), and rows made
-all ties (zero head weights), where the k lowest positions must win."""
+two shapes over a paged cache (pages scattered over the pool), 128 and 32
+indexer heads (one and two rows a wave), and rows made all ties (zero head
+weights), where the k lowest positions must win."""
 
 import numpy as np
 import pytest
@@ -28,6 +29,10 @@ CASES = {
                                               paged=True),
     "chunk_paged_3seq_k256": synth.Workload("fused_chunk_paged", 35, "chunk", 3, 0, ctx_range=(900, 2500),
                                             q_per_seq=40, top_k=256, heads=16, paged=True),
+    "prefill_h128_2000_k128": synth.Workload("fused_prefill_h128", 36, "prefill", 1, 2000, h_i=128, top_k=128,
+                                             heads=16),
+    "chunk_h32_paged_k64": synth.Workload("fused_chunk_h32", 37, "chunk", 3, 0, ctx_range=(700, 1800),
+                                          q_per_seq=24, h_i=32, top_k=64, heads=16, paged=True),
 }
 
 
