@@ -166,7 +166,7 @@ __device__ __forceinline__ void score_subtile(const uint8_t *stage_keys, const f
   }
 }
 
-template <int MT, int QW>
+template <int MT, int QW, bool PAGED>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
     BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k,
@@ -229,10 +229,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
     const int lim = max(min(row_n[j], s_end) - s_begin, 0);
     orow[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)t * ld + s_begin, 0, 4 * lim, 0x00020000);
   }
-  if (tid < kTPages) {
+  if (PAGED && tid < kTPages) {
     const int s = min(s_begin + kPageSize * tid, n_max - 1);
     sh.page_row[tid] = key_row(kd, b, s & ~(kPageSize - 1));
   }
+  const int64_t kbase = PAGED ? 0 : kd.k_seq_start[b];
+  // flat row of key s of the sequence (paged: through the block's page bases)
+  auto row_of = [&](int s) __attribute__((always_inline)) -> int64_t {
+    if constexpr (PAGED) return sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+    else return kbase + s;
+  };
   // The query, weight and page loads must be complete (and known complete
   // to the compiler) before the stage loads are issued: otherwise its wait
   // bookkeeping would later wait for them behind stage loads kept in flight.
@@ -254,12 +260,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_tiled_kernel(
       const int j = wave + 4 * m;
       const int r = 8 * j + (lane >> 3);
       const int s = min(s_stage + r, n_max - 1);
-      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      const int64_t row = row_of(s);
       lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kTStageBytes + 1024 * j);
     }
     if (wave < 2) {
       const int s = min(s_stage + 64 * wave + lane, n_max - 1);
-      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      const int64_t row = row_of(s);
       lds_dma4_at(k_scale + row, ksc0 + buf * (kTStageKeys * 4) + 256 * wave);
     }
   };
@@ -898,9 +904,15 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
     const int qw = h_i == 128 ? 1 : 2;
     const dim3 grid((max_k_len + kTKeysPerBlock - 1) / kTKeysPerBlock, (max_q_per_seq + 4 * qw - 1) / (4 * qw),
                     num_seqs);
-#define DSA_TILED(MT, QW)                                                                                    \
-  hipLaunchKernelGGL((indexer_fp8_tiled_kernel<MT, QW>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q, \
-                     q_scale, w, k, k_scale, scale, scores, ld)
+#define DSA_TILED(MT, QW)                                                                                       \
+  do {                                                                                                             \
+    if (kd.paged)                                                                                                  \
+      hipLaunchKernelGGL((indexer_fp8_tiled_kernel<MT, QW, true>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q, \
+                         q_scale, w, k, k_scale, scale, scores, ld);                                               \
+    else                                                                                                           \
+      hipLaunchKernelGGL((indexer_fp8_tiled_kernel<MT, QW, false>), grid, dim3(kIdxThreads), 0, stream, bt, kd,   \
+                         q, q_scale, w, k, k_scale, scale, scores, ld);                                            \
+  } while (0)
     switch (h_i) {
       case 32: DSA_TILED(1, 2); break;
       case 64: DSA_TILED(2, 2); break;
