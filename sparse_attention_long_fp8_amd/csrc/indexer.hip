@@ -726,7 +726,7 @@ struct IdxStagedLds {
   int64_t page_row[KPB / kPageSize];  // flat row of key 64p of the block (contiguous: s_begin + 64p)
 };
 
-template <int MT, int KPB>
+template <int MT, int KPB, bool PAGED>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
     BatchDev bt, KeysDev kd, const uint8_t *__restrict__ q, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k,
@@ -770,11 +770,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
     }
   const float row_scale = q_scale[t] * scale;
   float *out = scores + (int64_t)t * ld;
-  // page bases of the block (for the contiguous layout: rows of keys 64p)
-  if (threadIdx.x < kStagedPages) {
+  // page bases of the block (paged layout; a contiguous one addresses rows directly)
+  if (PAGED && threadIdx.x < kStagedPages) {
     const int s = min(s_begin + kPageSize * (int)threadIdx.x, n - 1);
     sh.page_row[threadIdx.x] = key_row(kd, b, s & ~(kPageSize - 1));
   }
+  const int64_t kbase = PAGED ? 0 : kd.k_seq_start[b];
+  auto row_of = [&](int s) __attribute__((always_inline)) -> int64_t {
+    if constexpr (PAGED) return sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+    else return kbase + s;
+  };
   // The query, weight and page loads must be complete (and known complete
   // to the compiler) before the stage loads are issued: otherwise its wait
   // bookkeeping would later wait for them behind stage loads kept in flight.
@@ -796,12 +801,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
       const int j = wave + 4 * m;
       const int r = 8 * j + (lane >> 3);
       const int s = min(s_stage + r, n - 1);
-      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      const int64_t row = row_of(s);
       lds_dma16_at(k + row * 128 + 16 * ((lane & 7) ^ kswz(r)), keys0 + buf * kDecStageBytes + 1024 * j);
     }
     if (wave < 2) {
       const int s = min(s_stage + 64 * wave + lane, n - 1);
-      const int64_t row = sh.page_row[(s - s_begin) >> kPageShift] + (s & (kPageSize - 1));
+      const int64_t row = row_of(s);
       lds_dma4_at(k_scale + row, ksc0 + buf * (kDecStageKeys * 4) + 256 * wave);
     }
   };
@@ -925,9 +930,15 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
   const bool one_round = (int64_t)((max_k_len + 2047) / 2048) * num_queries <= staged_resident(h_i);
   const int kpb = one_round ? 2048 : 1024;
   dim3 grid((max_k_len + kpb - 1) / kpb, num_queries);
-#define DSA_STAGED(MT, KPB)                                                                                  \
-  hipLaunchKernelGGL((indexer_fp8_staged_kernel<MT, KPB>), grid, dim3(kIdxThreads), 0, stream, bt, kd, q, \
-                     q_scale, w, k, k_scale, scale, scores, ld)
+#define DSA_STAGED(MT, KPB)                                                                                       \
+  do {                                                                                                            \
+    if (kd.paged)                                                                                                 \
+      hipLaunchKernelGGL((indexer_fp8_staged_kernel<MT, KPB, true>), grid, dim3(kIdxThreads), 0, stream, bt, kd, \
+                         q, q_scale, w, k, k_scale, scale, scores, ld);                                           \
+    else                                                                                                          \
+      hipLaunchKernelGGL((indexer_fp8_staged_kernel<MT, KPB, false>), grid, dim3(kIdxThreads), 0, stream, bt,    \
+                         kd, q, q_scale, w, k, k_scale, scale, scores, ld);                                       \
+  } while (0)
   switch (h_i) {
     case 32:
       if (one_round) DSA_STAGED(1, 2048); else DSA_STAGED(1, 1024);
