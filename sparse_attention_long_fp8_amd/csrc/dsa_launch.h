@@ -25,8 +25,8 @@ hipError_t launch_indexer_fp8(const BatchDev &bt, const KeysDev &kd, int num_seq
 // Fused indexer -> top-k (FP8, 32, 64 or 128 heads x 128; contiguous keys, or paged
 // histories of at most fused_topk_max_paged_keys keys): candidate list
 // capacity per row and workspace bytes.
-int fused_topk_cap(int k);
-size_t fused_topk_workspace_bytes(int num_queries, int k);
+int fused_topk_cap(int k, int max_k_len);
+size_t fused_topk_workspace_bytes(int num_queries, int k, int max_k_len);
 constexpr int fused_topk_max_paged_keys = 2048 * 64;
 hipError_t launch_indexer_topk_fused(const BatchDev &bt, const KeysDev &kd, int num_seqs, int num_queries,
                                      int max_q_per_seq, int max_k_len, int h_i, const uint8_t *q,

@@ -859,11 +859,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_staged_kernel(
   }
 }
 
-int fused_topk_cap(int k) { return (2 * k + kTStageKeys + 63) / 64 * 64; }
+// A row's list holds m*k + one stage of candidates, m growing with the
+// history: 2 up to 4096 keys, then one more per doubling, at most 8.  A
+// compaction re-reads the whole list (four radix passes and the ordered
+// rewrite); after one, about (m-1)*k new keys must beat the k-th score before
+// the next, and a row's k-th score rises so slowly that this takes a history
+// e^(m-1) times as long.  Longer lists make compactions rare but the final
+// selection larger: measured, m = 4 is fastest at 16384 keys and m = 6 at
+// 65536 (prefill_64k indexer + top-k 27.2 ms at m = 2, 22.2 ms at m = 6).
+int fused_topk_cap(int k, int max_k_len) {
+  int m = 2;
+  for (int len = 4096; len < max_k_len && m < 8; len *= 2) ++m;
+  return (int)(((int64_t)m * k + kTStageKeys + 63) / 64 * 64);
+}
 
-size_t fused_topk_workspace_bytes(int num_queries, int k) {
+size_t fused_topk_workspace_bytes(int num_queries, int k, int max_k_len) {
   // candidate scores, then candidate positions (each 256-byte aligned)
-  const size_t one = ((size_t)num_queries * fused_topk_cap(k) * 4 + 255) / 256 * 256;
+  const size_t one = ((size_t)num_queries * fused_topk_cap(k, max_k_len) * 4 + 255) / 256 * 256;
   return 2 * one;
 }
 
@@ -873,7 +885,7 @@ hipError_t launch_indexer_topk_fused(const BatchDev &bt, const KeysDev &kd, int 
                                      float scale, int topk, int32_t *indices, void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
   if (kd.paged && max_k_len > kFusedMaxPages * kPageSize) return hipErrorInvalidValue;
-  const int cap = fused_topk_cap(topk);
+  const int cap = fused_topk_cap(topk, max_k_len);
   const size_t one = ((size_t)num_queries * cap * 4 + 255) / 256 * 256;
   float *cand_s = (float *)workspace;
   int32_t *cand_i = (int32_t *)((char *)workspace + one);

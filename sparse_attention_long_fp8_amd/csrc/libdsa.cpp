@@ -162,7 +162,7 @@ bool fused_applies(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t
 // fp32 score rows the two separate stages pass between them.
 size_t indexer_topk_ws(const dsa_batch_t *bt, const dsa_kv_layout_t *ly, dsa_dtype_t dt, int32_t h_i, int32_t d_i,
                        int32_t k) {
-  if (fused_applies(bt, ly, dt, h_i, d_i)) return dsa::fused_topk_workspace_bytes(bt->num_queries, k);
+  if (fused_applies(bt, ly, dt, h_i, d_i)) return dsa::fused_topk_workspace_bytes(bt->num_queries, k, bt->max_k_len);
   return round_up((size_t)bt->num_queries * round_up((size_t)bt->max_k_len, 4) * sizeof(float), 256) +
          dsa::topk_workspace_bytes(bt->num_queries, bt->max_k_len, k);
 }
@@ -184,7 +184,7 @@ ForwardWs forward_ws(const dsa_forward_args_t *a) {
   size_t off = 0;
   w.scores_off = off;
   if (w.fused)
-    off += round_up(dsa::fused_topk_workspace_bytes(a->batch.num_queries, a->top_k), 256);
+    off += round_up(dsa::fused_topk_workspace_bytes(a->batch.num_queries, a->top_k, a->batch.max_k_len), 256);
   else if (!a->scores)
     off += round_up(T * (size_t)w.ld * sizeof(float), 256);
   w.indices_off = off;

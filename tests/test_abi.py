@@ -127,11 +127,15 @@ def test_workspace_sizes_and_too_small():
 
 def test_fused_indexer_topk_workspace_choice():
     """dsa_indexer_topk takes the fused kernel (candidate lists, 8 bytes per
-    entry, 2k + 128 entries rounded to 64 per row) for prefill batches with
+    entry, m*k + 128 entries rounded to 64 per row, m = 2 up to 4096 keys and
+    one more per doubling of the history, at most 8) for prefill batches with
     contiguous keys or paged histories up to 131072 keys; past that, and for
     decode batches, the two stages (fp32 score rows, then top-k's own)."""
     k = 2048
-    cap = (2 * k + 128 + 63) // 64 * 64
+
+    def cap(maxk):
+        m = {4096: 2, 4097: 3, 16384: 4, 65536: 6, 131072: 7, 140000: 8, 10 ** 6: 8}[maxk]
+        return (m * k + 128 + 63) // 64 * 64
 
     def r256(x):
         return -(-x // 256) * 256
@@ -146,11 +150,15 @@ def test_fused_indexer_topk_workspace_choice():
         return r256(T * (-(-maxk // 4) * 4) * 4) + B.dsa_topk_workspace_size(
             B.dsa_batch_t(T // maxq, T, 0x1000, 0x2000, maxq, maxk), k)
 
-    fused = 2 * r256(4096 * cap * 4)
-    assert ws(4096, 4096, 131072, False) == fused
-    assert ws(4096, 4096, 131072, True) == fused
+    def fused(maxk):
+        return 2 * r256(4096 * cap(maxk) * 4)
+
+    for maxk in (4096, 4097, 16384, 65536, 131072):
+        assert ws(4096, 4096, maxk, False) == fused(maxk), maxk
+    assert ws(4096, 4096, 131072, True) == fused(131072)
     assert ws(4096, 4096, 131073, True) == unfused(4096, 4096, 131073)
-    assert ws(4096, 4096, 140000, False) == fused            # contiguous keys: no length limit
+    assert ws(4096, 4096, 140000, False) == fused(140000)     # contiguous keys: no length limit
+    assert ws(4096, 4096, 10 ** 6, False) == fused(10 ** 6)   # m stops at 8
     assert ws(32, 1, 32768, False) == unfused(32, 1, 32768)   # decode rows: the two stages
 
 
