@@ -397,22 +397,42 @@ __device__ __forceinline__ void load_cands(const float *cs, int n, int i, uint32
 }
 
 // The k-th largest key among the n (> k) candidates of a list, and how many
-// candidates equal to it belong to the k best.  Whole wave; uniform results.
-__device__ void wave_select_kth(const float *cs, int n, int k, uint32_t *hist, uint32_t &tau, int &need_eq) {
+// candidates equal to it belong to the k best.  Every key lies in [lo, hi]
+// (bounds uniform over the wave), so the bits above the highest one where lo
+// and hi differ are common to every key and are decided before any pass; the
+// rest are resolved by radix passes of 8 bits from the top (a list's keys
+// share their leading bits, so this saves passes and spreads the first
+// digit over the histogram instead of piling it onto one bin).  Each pass
+// issues the loads of U chunks of 256 candidates before it uses them.  Whole
+// wave; uniform results.
+template <int U>
+__device__ void wave_select_kth(const float *cs, int n, int k, uint32_t lo, uint32_t hi, uint32_t *hist,
+                                uint32_t &tau, int &need_eq) {
   const int lane = lane_id();
-  uint32_t prefix = 0u, pmask = 0u;
+  if (lo == hi) {  // every key equal: the first k in list order
+    tau = lo;
+    need_eq = k;
+    return;
+  }
+  const int top = 31 - __builtin_clz(lo ^ hi);  // highest bit where keys may differ
+  uint32_t pmask = top == 31 ? 0u : ~0u << (top + 1);
+  uint32_t prefix = lo & pmask;
   int need = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int hb = top; hb >= 0; hb -= 8) {  // digit: bits hb .. shift
+    const int shift = hb >= 7 ? hb - 7 : 0;
+    const uint32_t dmask = (2u << (hb - shift)) - 1u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[lane + 64 * q] = 0u;
-    for (int i0 = 0; i0 < n; i0 += 256) {
-      uint32_t key[4];
-      bool valid[4];
-      load_cands(cs, n, i0 + 4 * lane, key, valid);
+    for (int i0 = 0; i0 < n; i0 += 256 * U) {
+      uint32_t key[U][4];
+      bool valid[U][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid[e] && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+      for (int u = 0; u < U; ++u) load_cands(cs, n, i0 + 256 * u + 4 * lane, key[u], valid[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (valid[u][e] && (key[u][e] & pmask) == prefix) atomicAdd(&hist[(key[u][e] >> shift) & dmask], 1u);
     }
     // lane l holds bins 255-4l .. 252-4l; scan them from the top
     int c[4], sl = 0;
@@ -443,7 +463,7 @@ __device__ void wave_select_kth(const float *cs, int n, int k, uint32_t *hist, u
     acc = __shfl(acc, L, 64);
     need -= acc;
     prefix |= (uint32_t)digit << shift;
-    pmask |= 0xFFu << shift;
+    pmask |= dmask << shift;
   }
   tau = prefix;
   need_eq = need;
@@ -550,10 +570,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
   // candidate lists of this wave's rows
   int cnt[QW];
   uint32_t tau[QW];
+  uint32_t klo[QW], khi[QW];  // this lane's bounds on the keys it appended (the list's: their wave min / max)
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     cnt[j] = 0;
     tau[j] = 0u;  // below every finite score's key
+    klo[j] = 0xFFFFFFFFu;
+    khi[j] = 0u;
   }
 
   // keep the k best of row j's list (final: write their positions to the
@@ -567,7 +590,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
     const bool all = n <= topk;
     uint32_t th = 0u;
     int need_eq = 0;
-    if (!all) wave_select_kth(cs, n, topk, sh.hist[wave], th, need_eq);
+    if (!all) {
+      uint32_t lo = klo[j], hi = khi[j];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+      }
+      if (final) wave_select_kth<4>(cs, n, topk, lo, hi, sh.hist[wave], th, need_eq);
+      else wave_select_kth<1>(cs, n, topk, lo, hi, sh.hist[wave], th, need_eq);
+    }
     int kept = 0, eq_seen = 0;
     for (int i0 = 0; i0 < n; i0 += 256) {
       const int i = i0 + 4 * lane;
@@ -624,6 +656,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       __threadfence_block();
       cnt[j] = kept;
       tau[j] = th;
+      klo[j] = th;  // every kept key is at least the k-th
     }
   };
 
@@ -640,12 +673,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) {
         const int s = held_s0 + 32 * sub + col;
-        const bool ok = half == 0 && s < row_n[j] && float_key(held[j][sub]) > tau[j];
+        const uint32_t key = float_key(held[j][sub]);
+        const bool ok = half == 0 && s < row_n[j] && key > tau[j];
         const uint64_t m = __ballot(ok);
         if (ok) {
           const int p = cnt[j] + lanes_below(m);
           cs[p] = held[j][sub];
           ci[p] = s;
+          klo[j] = min(klo[j], key);
+          khi[j] = max(khi[j], key);
         }
         cnt[j] += __popcll(m);
       }
