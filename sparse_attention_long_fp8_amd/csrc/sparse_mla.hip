@@ -406,15 +406,19 @@ struct MlaLds {
 
 // 128 heads: the P.V product is split over output columns (see the kernel),
 // which needs the P fragments, the rescale factors and the denominators in
-// LDS; three tile buffers leave the room.
+// LDS; three tile buffers leave the room.  The P exchange has two buffers
+// (tiles alternate), so a tile needs one barrier.
 constexpr int kBufsSplit = 3;
+struct MlaXchg {
+  v8bf p[8][64];     // P fragment of each wave's 16 heads, lane by lane
+  float alpha[128];  // rescale factor of each head (valid where resc is set)
+  int32_t resc[8];   // wave w rescaled its heads in this tile
+};
 struct MlaLdsSplit {
   uint8_t tile[kBufsSplit][kTileBytes];
   int32_t rows[kMaxSlots];
-  v8bf p[8][64];        // P fragment of each wave's 16 heads, lane by lane
-  float alpha[128];     // rescale factor of each head (valid where resc is set)
-  int32_t resc[8];      // wave w rescaled its heads in this tile
-  float inv_l[128];     // 1 / denominator of each head
+  MlaXchg x[2];      // exchange buffers of even and odd tiles
+  float inv_l[128];  // 1 / denominator of each head
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -583,14 +587,21 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   // before the tile loop: otherwise its wait bookkeeping re-waits for them in
   // every iteration, draining the tile loads kept in flight.  They complete
   // together with tile 0's gather; the next tiles go out after.
+  // 128 heads fill all NB buffers here and refill a buffer right after the
+  // tile's barrier (see below); the others keep one buffer for the gather at
+  // the top of each tile.
+  constexpr int kAhead = kSplit ? NB : NB - 1;
   if (nblk > 0) gather(0, 0);
   wait_vmcnt<0>();
-  for (int p = 1; p < NB - 1 && p < nblk; ++p) gather(p, p);
+  for (int p = 1; p < kAhead && p < nblk; ++p) gather(p, p);
   lds_barrier();
 
   for (int blk = 0; blk < nblk; ++blk) {
     const int buf = blk % NB;
-    if (blk + NB - 1 < nblk) gather(blk + NB - 1, (blk + NB - 1) % NB);
+    if (!kSplit && blk + NB - 1 < nblk) gather(blk + NB - 1, (blk + NB - 1) % NB);
+    // 128 heads: the buffer of tile blk-1, free since the last barrier, takes
+    // tile blk-1+NB
+    if (kSplit && blk >= 1 && blk - 1 + NB < nblk) gather(blk - 1 + NB, (blk - 1) % NB);
     const uint8_t *tile = sh.tile[buf];
     const int32_t *rows = sh.rows + blk * kBlk;
 
@@ -684,39 +695,53 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       l_part[ht] = l_part[ht] * alpha[ht] + sum;
     }
     if constexpr (kSplit) {
-      // this wave's P fragment, rescale flag and factors go to LDS; after the
-      // barrier every wave reads all eight
-      *(v8bf *)&sh.p[wave][lane] = pf[0];
-      const bool any = __ballot(rescale) != 0;
-      if (lane == 0) sh.resc[wave] = any;
-      if (any) {  // (its address is computed here: a register held across the loop would spill)
-        const int ln = opaque_lane_id();
-        if (ln < 16) sh.alpha[16 * wave + ln] = alpha[0];
-      }
-      lds_barrier();
-      // ---- O[all heads, dims 64w..64w+63] += P . V ----
       // V fragments of the wave's four dim tiles (transpose reads, as below),
-      // then each head tile's P from LDS
-      const uint8_t *vrow = tile + tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+      // read before the barrier: after it no wave reads this tile's buffer,
+      // which is refilled at once.  The lane's offset is made opaque in each
+      // tile, so the eight reads share one address register (immediate
+      // offsets) instead of eight hoisted out of the loop.
+      int voff = tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3) + 32 * kOt * wave;
+      __asm__ volatile("" : "+v"(voff));
+      const uint8_t *vrow = tile + voff;
       v8bf vb[kOt];
 #pragma unroll
       for (int j = 0; j < kOt; ++j) {
-        const int nt = kOt * wave + j;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * j));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * j));
         __builtin_memcpy(&vb[j], &lo, 8);
         __builtin_memcpy((char *)&vb[j] + 8, &hi, 8);
       }
+      // this wave's P fragment, rescale flag and factors go to this tile's
+      // exchange buffer; after the barrier every wave reads all eight
+      MlaXchg &xc = sh.x[blk & 1];
+      *(v8bf *)&xc.p[wave][lane] = pf[0];
+      const bool any = __ballot(rescale) != 0;
+      if (lane == 0) xc.resc[wave] = any;
+      if (any) {  // (its address is computed here: a register held across the loop would spill)
+        const int ln = opaque_lane_id();
+        if (ln < 16) xc.alpha[16 * wave + ln] = alpha[0];
+      }
+      // One barrier a tile.  Before it: the next tile has landed (this wave's
+      // share of it; tile blk+2 may stay in flight).  After it: the next tile
+      // and this tile's P are visible to every wave, and every wave is done
+      // with this tile's buffer (QK operands and V fragments), which takes
+      // tile blk+NB at the top of the next tile.  The exchange
+      // buffer is written again for tile blk+2, after the next barrier,
+      // which every wave reaches only once its P.V product of this tile has
+      // read it.
+      wait_tiles(min(nblk - 1, blk + NB - 1) - (blk + 1));
+      lds_barrier();
+      // ---- O[all heads, dims 64w..64w+63] += P . V ----
       // rescales first, behind one wave-uniform branch (rare), so that the
       // products below are one block in which P reads run ahead of the MFMAs
-      const v4i rf0 = *(const v4i *)&sh.resc[0], rf1 = *(const v4i *)&sh.resc[4];
+      const v4i rf0 = *(const v4i *)&xc.resc[0], rf1 = *(const v4i *)&xc.resc[4];
       if ((rf0.x | rf0.y | rf0.z | rf0.w | rf1.x | rf1.y | rf1.z | rf1.w) != 0) {
 #pragma unroll
         for (int a = 0; a < kOh; ++a) {
           if ((a < 4 ? rf0[a & 3] : rf1[a & 3]) != 0) {
             float r[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = sh.alpha[16 * a + 4 * g + i];
+            for (int i = 0; i < 4; ++i) r[i] = xc.alpha[16 * a + 4 * g + i];
 #pragma unroll
             for (int j = 0; j < kOt; ++j)
 #pragma unroll
@@ -724,11 +749,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
           }
         }
       }
-      v8bf pa = sh.p[0][lane];
+      v8bf pa = xc.p[0][lane];
 #pragma unroll
       for (int a = 0; a < kOh; ++a) {
         v8bf pn;
-        if (a + 1 < kOh) pn = sh.p[a + 1][lane];  // one head tile ahead
+        if (a + 1 < kOh) pn = xc.p[a + 1][lane];  // one head tile ahead
 #pragma unroll
         for (int j = 0; j < kOt; ++j) o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[j], o[a][j], 0, 0, 0);
         if (a + 1 < kOh) pa = pn;
@@ -780,9 +805,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, DSA_PV_AHEAD * HT, 0);
     }
 
-    // the next tile must have landed; the ones after it may stay in flight
-    wait_tiles(min(nblk - 1, blk + NB - 1) - (blk + 1));
-    lds_barrier();
+    if constexpr (!kSplit) {
+      // the next tile must have landed; the ones after it may stay in flight
+      wait_tiles(min(nblk - 1, blk + NB - 1) - (blk + 1));
+      lds_barrier();
+    }
   }
 
   // ---- finish: denominators, output ----
