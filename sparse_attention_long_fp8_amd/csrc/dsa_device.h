@@ -115,6 +115,27 @@ __device__ __forceinline__ void lds_dma16_at(const void *gaddr, uint32_t lds_byt
       : "memory");
 }
 
+// The same load from gaddr + OFF, OFF an immediate byte offset in the
+// instruction (0 <= OFF < 4096), so that loads from one per-lane base need no
+// address arithmetic of their own.  The instruction adds OFF to the LDS
+// address as well (pinned by a probe), so M0 is set to lds_byte - OFF: lane
+// i's 16 bytes still land at lds_byte + 16 * i.  Needs lds_byte >= OFF.
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_imm(const void *gaddr, uint32_t lds_byte) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte) - (uint32_t)OFF;
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off offset:%3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(gaddr), "n"(OFF)
+      : "memory");
+}
+
 // The same 16-byte load from one wave-uniform base address: lane i's 16
 // bytes come from sbase + voff (voff a per-lane byte offset) and land at LDS
 // byte address lds_byte + 16 * i.  The base is held in scalar registers, so

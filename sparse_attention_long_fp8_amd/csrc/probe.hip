@@ -1,7 +1,7 @@
 // Test-only probes of gfx950 instruction semantics the libdsa kernels rely
 // on: FP8, bf16 and fp32 MFMA operand / accumulator lane layouts (and with them the
-// FP8 E4M3 interpretation of bytes) and the lane mapping of the LDS transpose
-// read.  One wave each, fully in bounds; built into libdsa_probe.so, which
+// FP8 E4M3 interpretation of bytes), the lane mapping of the LDS transpose
+// read, and where an LDS-DMA load with an immediate offset writes.  One wave each, fully in bounds; built into libdsa_probe.so, which
 // only the test-suite loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,6 +56,35 @@ __global__ void probe_tr16_kernel(const short *src, const int *off, v4s *dst) {
   dst[threadIdx.x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((char *)lds + o));
 }
 
+// One wave's 16-byte global -> LDS load (global_load_lds_dwordx4) with a
+// 256-byte immediate offset in the instruction and M0 = the LDS buffer's base.
+// src holds 2048 bytes (lane l reads src + 16 l + 256, inside them); the 4 KB
+// LDS buffer is zeroed before the load and copied to dst (4096 bytes) after
+// it, so that the caller sees where the wave's 1 KB landed: at 16 l, or at
+// 16 l + 256 if the immediate offsets the LDS address too.  Either way every
+// byte written lies inside the buffer.
+__global__ void probe_dma_offset_kernel(const uint8_t *src, int4 *dst) {
+  __shared__ int4 lds[256];
+  for (int i = threadIdx.x; i < 256; i += 64) lds[i] = int4{0, 0, 0, 0};
+  __syncthreads();
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds);
+  const uint8_t *g = src + 16 * threadIdx.x;
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off offset:256\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(g)
+      : "memory");
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += 64) dst[i] = lds[i];
+}
+
 // Plain 16-byte-per-lane copy: the known-size reference that HBM traffic
 // counters of the other kernels are scaled by.
 __global__ void copy_kernel(const int4 *src, int4 *dst, long long n16) {
@@ -103,6 +132,12 @@ int dsa_probe_tr16(const void *src, const int *off_host, const int *off_dev, voi
     if (off_host[i] < 0 || off_host[i] > 8192 - 8 || (off_host[i] & 7)) return -1;
   hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, stream, (const short *)src, off_dev,
                      (v4s *)dst);
+  return (int)hipGetLastError();
+}
+
+// src: 2048 bytes, dst: 4096 bytes (device); see probe_dma_offset_kernel.
+int dsa_probe_dma_offset(const void *src, void *dst, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_dma_offset_kernel, dim3(1), dim3(64), 0, stream, (const uint8_t *)src, (int4 *)dst);
   return (int)hipGetLastError();
 }
 

@@ -15,6 +15,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // eight independent fp32 FMAs (x[i] += m1 * m2), written out so that the
 // compiler can neither merge nor drop them
@@ -90,21 +92,137 @@ __global__ __launch_bounds__(1024) void lds_rate_kernel(float *out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x + acc.y + acc.z + acc.w);
 }
 
+// LDS reads in the access patterns of the attention kernel's tile (rows of
+// 1040 bytes; 32 tokens), eight per thread and iteration, every address inside
+// the 64 KB buffer:
+//   P = 0: 16-byte reads, lane l at byte 16 l of a 1 KB block (the plain case);
+//   P = 1: 16-byte QK operand reads: lane (g = l / 16, m = l % 16) reads token
+//          tok(m) of a 16-token half at byte 16 g + 64 ks (ks = 0 .. 15);
+//   P = 2: the same with token m (no permutation);
+//   P = 3: 8-byte reads, lane l at byte 8 l of a 512-byte block (plain);
+//   P = 4: 8-byte transpose reads of the P.V product: lane (g, n) reads token
+//          tok(4 g + n / 4) at byte 8 (n % 4) + 32 nt (nt = 0 .. 31).
+__device__ __forceinline__ int probe_tok(int m) { return 4 * (m & 3) + (((m >> 1) & 2) | ((m >> 3) & 1)); }
+
+template <int P>
+__global__ __launch_bounds__(1024) void lds_pattern_kernel(float *out, int iters) {
+  __shared__ v4i buf[4096];  // 64 KB
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = v4i{i, i + 1, i + 2, i + 3};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  const uint8_t *base = (const uint8_t *)buf + (wave & 1) * 32768;  // two tiles' worth
+  int off;
+  if constexpr (P == 0) off = 16 * lane;
+  else if constexpr (P == 1) off = probe_tok(n) * 1040 + 16 * g;
+  else if constexpr (P == 2) off = n * 1040 + 16 * g;
+  else if constexpr (P == 3) off = 8 * lane;
+  else off = probe_tok(4 * g + (n >> 2)) * 1040 + 8 * (n & 3);
+  // the second iteration's reads sit `step` bytes further; the offset is made
+  // opaque in every iteration so that the loads are not hoisted out of the loop
+  constexpr int step = P == 0 ? 8192 : P == 4 ? 128 : 256;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    int o = off + (it & 1) * step;
+    __asm__ volatile("" : "+v"(o));
+    const uint8_t *b = base + o;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if constexpr (P == 0) {
+        acc += *(const v4i *)(b + 1024 * r);
+      } else if constexpr (P == 1 || P == 2) {
+        acc += *(const v4i *)(b + 16 * 1040 * (r & 1) + 64 * (r >> 1));
+      } else if constexpr (P == 3) {
+        const int2 v = *(const int2 *)(b + 4096 * r);  // (the compiler pairs them: ds_read2st64_b64)
+        acc.x += v.x;
+        acc.y += v.y;
+      } else {
+        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(b + 16 * 1040 * (r & 1) + 32 * (r >> 1)));
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x + acc.y + acc.z + acc.w);
+}
+
+// LDS reads at per-lane offsets from a table: read r (0..7) of lane l is at
+// byte tab[64 r + l] of a 32 KB half of the buffer (waves alternate halves),
+// plus `step` bytes in odd iterations.  W = 16: 16-byte reads; W = 8: 8-byte
+// transpose reads (ds_read_tr16_b64).  The host keeps every offset + step + W
+// within 32 KB and aligned to W.
+template <int W>
+__global__ __launch_bounds__(1024) void lds_table_kernel(float *out, const int *__restrict__ tab, int iters, int step) {
+  __shared__ v4i buf[4096];  // 64 KB
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = v4i{i, i + 1, i + 2, i + 3};
+  const int lane = threadIdx.x & 63;
+  int offs[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) offs[r] = tab[64 * r + lane];
+  __syncthreads();
+  const uint8_t *base = (const uint8_t *)buf + ((threadIdx.x >> 6) & 1) * 32768;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    int o = (it & 1) * step;
+    __asm__ volatile("" : "+v"(o));
+    const uint8_t *b = base + o;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if constexpr (W == 16) {
+        acc += *(const v4i *)(b + offs[r]);
+      } else {
+        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(b + offs[r]));
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x + acc.y + acc.z + acc.w);
+}
+
 }  // namespace
 
 extern "C" {
 
+// LDS reads at the offsets of `tab` (512 ints on the device, see
+// lds_table_kernel): width 16 or 8 (transpose reads); threads 256, 512 or
+// 1024; blocks <= 4096; out holds blocks x threads floats.  The caller keeps
+// every offset + step + width within 32768 and aligned to the width.  Returns
+// 0, or -1 for an unsupported combination (nothing launched).
+int dsa_probe_lds_table(int width, const int *tab, int step, int blocks, int threads, int iters, float *out,
+                        hipStream_t stream) {
+  if (blocks < 1 || blocks > 4096 || iters < 1 || step < 0 || (threads != 256 && threads != 512 && threads != 1024))
+    return -1;
+  if (width == 16) hipLaunchKernelGGL(lds_table_kernel<16>, dim3(blocks), dim3(threads), 0, stream, out, tab, iters, step);
+  else if (width == 8) hipLaunchKernelGGL(lds_table_kernel<8>, dim3(blocks), dim3(threads), 0, stream, out, tab, iters, step);
+  else return -1;
+  return (int)hipGetLastError();
+}
+
 // kind 0-2: MFMA rate probes (see rate_kernel) with `valu` in {0, 16, 32}
 // VALU FMAs per MFMA (kind 2) or 0 (kinds 0, 1); kind 3: VALU only, 64 FMAs
-// per iteration; kind 4: LDS reads (threads = 256, 512 or 1024 per block).
+// per iteration; kind 4: LDS reads (threads = 256, 512 or 1024 per block);
+// kinds 5-9: LDS reads in pattern 0-4 of lds_pattern_kernel (same threads).
 // blocks <= 4096; out holds blocks x 1024 floats.  Returns 0, or -1 for an
 // unsupported combination (nothing launched).
 int dsa_probe_rate(int kind, int valu, int blocks, int threads, int iters, float *out, hipStream_t stream) {
   if (blocks < 1 || blocks > 4096 || iters < 1) return -1;
   const dim3 g(blocks), b(256);
-  if (kind == 4) {
+  if (kind >= 4 && kind <= 9) {
     if (threads != 256 && threads != 512 && threads != 1024) return -1;
-    hipLaunchKernelGGL(lds_rate_kernel, g, dim3(threads), 0, stream, out, iters);
+    const dim3 b(threads);
+    switch (kind) {
+      case 4: hipLaunchKernelGGL(lds_rate_kernel, g, b, 0, stream, out, iters); break;
+      case 5: hipLaunchKernelGGL(lds_pattern_kernel<0>, g, b, 0, stream, out, iters); break;
+      case 6: hipLaunchKernelGGL(lds_pattern_kernel<1>, g, b, 0, stream, out, iters); break;
+      case 7: hipLaunchKernelGGL(lds_pattern_kernel<2>, g, b, 0, stream, out, iters); break;
+      case 8: hipLaunchKernelGGL(lds_pattern_kernel<3>, g, b, 0, stream, out, iters); break;
+      default: hipLaunchKernelGGL(lds_pattern_kernel<4>, g, b, 0, stream, out, iters); break;
+    }
     return (int)hipGetLastError();
   }
   if (threads != 256) return -1;

@@ -12,6 +12,7 @@
 #include <hip/hip_bf16.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "dsa_device.h"
 #include "dsa_launch.h"
@@ -340,20 +341,20 @@ __global__ __launch_bounds__(256) void mla_f32_combine_kernel(int heads, int d_v
 //   * rows: every slot of the range is resolved once (index -> page -> row)
 //     into LDS before the tile loop, so the loop issues no dependent loads;
 //   * gather: the 32 selected 1152-byte key rows of a tile go straight into
-//     LDS with 16-byte global->LDS loads: each row's 1024-byte latent part at
-//     a 1040-byte pitch (one wave-wide load from a scalar base address), the
-//     32 128-byte rotary parts after them, their 16-byte chunks XOR-permuted
-//     by the row (8 rows a load).  A tile is exactly 36 wave-wide loads, spread
-//     over the waves with the same count for every tile, so a per-wave vmcnt
-//     wait retires exactly the tile that is needed next; three (128 heads) or
-//     four tile buffers keep the next tiles in flight while one is computed;
+//     LDS with 16-byte global->LDS loads, column-major in 16-byte chunks
+//     (chunk c of token t at 512 c + 16 t), two chunk columns a wave-wide
+//     load, each lane loading from its own token's row.  A tile is exactly 36
+//     wave-wide loads, spread over the waves with the same count for every
+//     tile, so a per-wave vmcnt wait retires exactly the tile that is needed
+//     next; three (128 heads) or four tile buffers keep the next tiles in
+//     flight while one is computed;
 //   * S^T[32 tok x 16 heads] = KV_tile[32 x 576] . Q^T[576 x 16] per head
 //       tile (16x16x32 bf16 MFMA; the query is the B operand, held in
 //       registers for the whole launch; each LDS fragment feeds every head
-//       tile of the wave).  A-operand row m of each 16-token half is token
-//       tok_of(m) (a fixed permutation, below), so that the value reads of
-//       the PV product, which follow the accumulator's token order, meet
-//       distinct LDS banks at the 1040-byte pitch;
+//       tile of the wave).  Sixteen lanes read one chunk of sixteen tokens:
+//       256 contiguous bytes.  A-operand row m of each 16-token half is token
+//       tok_of(m) (a fixed permutation, below), the order in which the
+//       value reads of the PV product follow the accumulator;
 //   * online softmax per head in the exp2 domain.  A head's reference max
 //     only moves when a tile's max exceeds it by more than 8 (so the
 //     unnormalised terms stay below 2^8); only then are its O rows and
@@ -376,19 +377,26 @@ constexpr int kNt = kDv / 16;                  // 32 output dim tiles
 constexpr int kBlk = 32;                       // selected tokens per tile
 constexpr int kMaxSlots = 2048;                // slots one workgroup resolves
 constexpr int kRowBytes = kD * 2;              // 1152
-constexpr int kLatBytes = kDv * 2;             // 1024: one wave-wide 16-byte load
-constexpr int kLatStride = kLatBytes + 16;     // LDS pitch of the latent parts
-constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128
-constexpr int kRopeOff = kBlk * kLatStride;    // rotary parts follow the latent parts
-// Token of A-operand row m (0..15) of a 16-token half of the QK product.  Lane
-// group g of a PV value read then addresses tokens 4r + (g with its two bits
-// swapped), r = 0..3: in each half-wave the eight rows sit 8 banks apart at the
-// 1040-byte pitch (4 banks a row), so the 32 lanes' 8-byte reads of 4 chunks a
-// row cover the 64 banks once.
+// Tile layout, column-major in 16-byte chunks: chunk c (dims 8c .. 8c+7) of
+// token t sits at byte kColBytes * c + 16 * t.  Sixteen lanes reading one
+// chunk of sixteen tokens then read 256 contiguous bytes, which LDS serves at
+// its full rate; a row-major tile (any row pitch tried) serves that QK operand
+// pattern at half the rate.
+constexpr int kChunks = kRowBytes / 16;        // 72 chunks a row
+constexpr int kColBytes = kBlk * 16;           // 512: one chunk of the 32 tokens
+constexpr int kTileBytes = kChunks * kColBytes;  // 36864
+constexpr int kTileLoads = kTileBytes / 1024;  // 36 wave-wide 1 KB loads per tile
+// Token of A-operand row m (0..15) of a 16-token half of the QK product.  The
+// S^T accumulator then holds tokens 4i + rho(g) in lane group g, the order in
+// which the P.V product's value reads proceed.
 __device__ __forceinline__ int tok_of(int m) { return 4 * (m & 3) + (((m >> 1) & 2) | ((m >> 3) & 1)); }
-constexpr int kTileBytes = kRopeOff + kBlk * kRopeBytes;
-constexpr int kRopeLoads = kBlk * kRopeBytes / 1024;  // 4: eight rows' rotary parts each
-constexpr int kTileLoads = kBlk + kRopeLoads;  // 36 wave-wide 1 KB loads per tile
+
+// f(integral_constant<int, I>) for each I of the sequence, in order (a loop
+// whose index must be a compile-time constant, e.g. an immediate offset).
+template <int... I, class F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, I...>, F &&f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 constexpr int kBufs = 4;                       // tile buffers: one computed, three in flight
 constexpr float kRefSlack = 8.f;               // log2 headroom above the reference max
 #ifndef DSA_QK_AHEAD
@@ -397,7 +405,7 @@ constexpr float kRefSlack = 8.f;               // log2 headroom above the refere
 #ifndef DSA_PV_AHEAD
 #define DSA_PV_AHEAD 3  // V fragments read ahead of the P.V MFMAs
 #endif
-static_assert(kRopeLoads * 8 == kBlk, "a rotary load covers eight rows");
+static_assert(kColBytes * 2 == 1024, "a wave-wide load fills two chunk columns");
 
 struct MlaLds {
   uint8_t tile[kBufs][kTileBytes];
@@ -511,49 +519,24 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   }
   lds_barrier();  // LDS only: the query loads stay in flight
 
-  // tile blk -> buffer buf, in 36 wave-wide 1 KB loads:
-  //   * latent loads: the first 1024 bytes of row j of the tile go to LDS
-  //     offset j * kLatStride, all 64 lanes from that one row, so the row's
-  //     address is wave-uniform and lives in scalar registers; wave w takes
-  //     rows kBlk/NW * w .. + kBlk/NW - 1 (their resolved rows come in 16-byte
-  //     LDS reads);
-  //   * rotary loads: the last 128 bytes of rows 8q .. 8q+7 go to kRopeOff +
-  //     q * 1024, lane l taking row 8q + l/8; wave w takes q = w, w + NW, ...
-  //     Lane l's LDS position l % 8 of its row r holds rotary chunk
-  //     (l % 8) ^ (r % 8), so sixteen rows read at one chunk spread over the
-  //     LDS banks.
-  // Masked slots load row0 (their logits are discarded).
-  constexpr int kLatPer = kBlk / NW;
-  static_assert(kLatPer % 4 == 0, "latent rows come in groups of four");
+  // tile blk -> buffer buf, in 36 wave-wide 1 KB loads: load L fills chunk
+  // columns 2L and 2L+1, lane i taking token i % 32, chunk 2L + i / 32 (its
+  // 16 bytes land at 16 i of the load's 1 KB, as the layout wants).  A lane's
+  // global address is its token's row plus 16 (i / 32), the same for every
+  // load of the tile, and load L adds 32 L as an immediate offset.  Wave w
+  // issues loads w, w + NW, ...  Masked slots load row0 (their logits are
+  // discarded).
   const bool hi = wave < kTileLoads % NW;  // waves that issue kLHi loads a tile
   auto gather = [&](int blk, int buf) __attribute__((always_inline)) {
-    const int32_t *rows = sh.rows + blk * kBlk;
-    const uint32_t tb = lds_addr(&sh.tile[buf][0]);
-#pragma unroll
-    for (int i0 = 0; i0 < kLatPer; i0 += 4) {
-      const int j0 = kLatPer * wave + i0;
-      const v4i r4 = *(const v4i *)(rows + j0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int row = __builtin_amdgcn_readfirstlane(r4[u]);
-        if (row < 0) row = (int)row0;
-        lds_dma16_sbase(kv_bytes + (int64_t)row * kRowBytes, 16u * lane, tb + (j0 + u) * kLatStride);
-      }
-    }
-#pragma unroll
-    for (int q0 = 0; q0 < kRopeLoads; q0 += NW) {
-      const int q = q0 + wave;
-      if (q < kRopeLoads) {
-        // the lane index is re-read here (two instructions) rather than kept:
-        // a loop-invariant address would be held in a register the tile loop
-        // does not have
-        const int ln = opaque_lane_id();
-        int row = rows[8 * q + (ln >> 3)];
-        if (row < 0) row = (int)row0;
-        lds_dma16_at(kv_bytes + (int64_t)row * kRowBytes + kLatBytes + 16 * ((ln & 7) ^ (ln >> 3)),
-                     tb + kRopeOff + q * 1024);
-      }
-    }
+    const int ln = opaque_lane_id();
+    int row = sh.rows[blk * kBlk + (ln & 31)];
+    if (row < 0) row = (int)row0;
+    const uint8_t *src = kv_bytes + (int64_t)row * kRowBytes + 16 * (ln >> 5) + 32 * wave;
+    const uint32_t tb = lds_addr(&sh.tile[buf][0]) + 1024 * wave;
+    for_each_index(std::make_integer_sequence<int, kLHi>{}, [&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      if (u < kLLo || hi) lds_dma16_imm<32 * NW * u>(src, tb + 1024 * NW * u);
+    });
   };
   // wait until at most `n` tiles of this wave's loads are still in flight
   auto wait_tiles = [&](int n) __attribute__((always_inline)) {
@@ -612,17 +595,13 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       s0[ht] = v4f{0.f, 0.f, 0.f, 0.f};
       s1[ht] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    // A fragments: K-steps 0-15 from the latent parts, 16-17 from the
-    // rotary parts (chunk c of row r at position c ^ (r % 8))
-    const int ar = tok_of(n16);  // A-operand row n16 is this token of each half
-    const uint8_t *alat = tile + ar * kLatStride + 16 * g;
-    const uint8_t *arope = tile + kRopeOff + ar * kRopeBytes;
+    // A fragments: lane (g, n16) reads chunk 4 ks + g of token tok_of(n16)
+    // of each 16-token half (K-steps 16-17 are the rotary dims)
+    const uint8_t *abase = tile + kColBytes * g + 16 * tok_of(n16);
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      const int ro = 16 * ((4 * (ks - kKsLat) + g) ^ (ar & 7));
-      const v8bf a0 = ks < kKsLat ? *(const v8bf *)(alat + 64 * ks) : *(const v8bf *)(arope + ro);
-      const v8bf a1 = ks < kKsLat ? *(const v8bf *)(alat + 16 * kLatStride + 64 * ks)
-                                  : *(const v8bf *)(arope + 16 * kRopeBytes + ro);
+      const v8bf a0 = *(const v8bf *)(abase + 4 * kColBytes * ks);
+      const v8bf a1 = *(const v8bf *)(abase + 256 + 4 * kColBytes * ks);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         s0[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ht][ks], s0[ht], 0, 0, 0);
@@ -700,14 +679,15 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       // which is refilled at once.  The lane's offset is made opaque in each
       // tile, so the eight reads share one address register (immediate
       // offsets) instead of eight hoisted out of the loop.
-      int voff = tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3) + 32 * kOt * wave;
+      int voff = 16 * tok_of(4 * g + (n16 >> 2)) + kColBytes * ((n16 >> 1) & 1) + 8 * (n16 & 1) +
+                 2 * kColBytes * kOt * wave;
       __asm__ volatile("" : "+v"(voff));
       const uint8_t *vrow = tile + voff;
       v8bf vb[kOt];
 #pragma unroll
       for (int j = 0; j < kOt; ++j) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * j));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * j));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 2 * kColBytes * j));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 256 + 2 * kColBytes * j));
         __builtin_memcpy(&vb[j], &lo, 8);
         __builtin_memcpy((char *)&vb[j] + 8, &hi, 8);
       }
@@ -783,11 +763,11 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       // inside a 16-lane group, lane i names 8 bytes of row i/4 (dims 4*(i%4)..+3
       // of a 16-dim tile); the transpose read hands lane i column i of the four
       // rows: 4 consecutive tokens of one dim, the B-operand slot order
-      const uint8_t *vrow = tile + tok_of(4 * g + (n16 >> 2)) * kLatStride + 8 * (n16 & 3);
+      const uint8_t *vrow = tile + 16 * tok_of(4 * g + (n16 >> 2)) + kColBytes * ((n16 >> 1) & 1) + 8 * (n16 & 1);
   #pragma unroll
       for (int nt = 0; nt < kNt; ++nt) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 32 * nt));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 16 * kLatStride + 32 * nt));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 2 * kColBytes * nt));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vrow + 256 + 2 * kColBytes * nt));
         v8bf vb;
         __builtin_memcpy(&vb, &lo, 8);
         __builtin_memcpy((char *)&vb + 8, &hi, 8);

@@ -1,6 +1,7 @@
 """Instruction-level probes on the GPU: the FP8, bf16 and fp32 MFMA operand and
 accumulator lane layouts the kernels rely on (with them the OCP E4M3
-reading of FP8 bytes), and the lane map of the LDS transpose read."""
+reading of FP8 bytes), the lane map of the LDS transpose read, and where a
+global -> LDS load with an immediate offset writes."""
 
 import ctypes
 import os
@@ -24,6 +25,7 @@ def probe(gpu):
                  "dsa_probe_f32_16x16x4"):
         getattr(lib, name).argtypes = [ctypes.c_void_p] * 4
     lib.dsa_probe_tr16.argtypes = [ctypes.c_void_p] * 5
+    lib.dsa_probe_dma_offset.argtypes = [ctypes.c_void_p] * 3
     return lib
 
 
@@ -187,3 +189,19 @@ def test_lds_transpose_read_lane_map(probe, gpu):
     got = dst.cpu().numpy()
     want = np.array([[64 * (l // 16) + 16 * r + l % 16 for r in range(4)] for l in range(64)])
     assert np.array_equal(got, want)
+
+
+def test_lds_dma_immediate_offset(probe, gpu):
+    """global_load_lds_dwordx4 with M0 = the LDS buffer and an immediate offset
+    of 256: lane l's 16 bytes come from src + 256 + 16 l and land at LDS byte
+    256 + 16 l -- the immediate moves the LDS address as well as the global
+    one, which the attention gather compensates for in M0."""
+    src = torch.arange(512, dtype=torch.int32).view(torch.uint8).to(gpu)
+    dst = torch.zeros(4096, dtype=torch.uint8, device=gpu)
+    assert probe.dsa_probe_dma_offset(src.data_ptr(), dst.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    want = src.cpu().numpy()[256:1280]
+    at0 = np.array_equal(got[:1024], want) and not got[1024:].any()
+    at256 = np.array_equal(got[256:1280], want) and not got[:256].any() and not got[1280:].any()
+    assert at256 and not at0
