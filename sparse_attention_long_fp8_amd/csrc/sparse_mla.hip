@@ -582,9 +582,6 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   for (int blk = 0; blk < nblk; ++blk) {
     const int buf = blk % NB;
     if (!kSplit && blk + NB - 1 < nblk) gather(blk + NB - 1, (blk + NB - 1) % NB);
-    // 128 heads: the buffer of tile blk-1, free since the last barrier, takes
-    // tile blk-1+NB
-    if (kSplit && blk >= 1 && blk - 1 + NB < nblk) gather(blk - 1 + NB, (blk - 1) % NB);
     const uint8_t *tile = sh.tile[buf];
     const int32_t *rows = sh.rows + blk * kBlk;
 
@@ -711,6 +708,14 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
       // read it.
       wait_tiles(min(nblk - 1, blk + NB - 1) - (blk + 1));
       lds_barrier();
+      // This tile's buffer is free: it takes tile blk+NB, whose loads go out
+      // one between each two head tiles of the P.V product below (all eight
+      // waves issuing their loads at once queue them in the CU's address
+      // unit for hundreds of clocks).  The row index is read first, so that
+      // its LDS latency passes under the first products.
+      const bool refill = blk + NB < nblk;
+      int rrow = 0;
+      if (refill) rrow = sh.rows[(blk + NB) * kBlk + (opaque_lane_id() & 31)];
       // ---- O[all heads, dims 64w..64w+63] += P . V ----
       // rescales first, behind one wave-uniform branch (rare), so that the
       // products below are one block in which P reads run ahead of the MFMAs
@@ -730,14 +735,27 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
         }
       }
       v8bf pa = xc.p[0][lane];
-#pragma unroll
-      for (int a = 0; a < kOh; ++a) {
+      const uint8_t *rsrc = kv_bytes;
+      const uint32_t rtb = lds_addr(&sh.tile[buf][0]) + 1024 * wave;
+      for_each_index(std::make_integer_sequence<int, kOh>{}, [&](auto ac) __attribute__((always_inline)) {
+        constexpr int a = decltype(ac)::value;
         v8bf pn;
         if (a + 1 < kOh) pn = xc.p[a + 1][lane];  // one head tile ahead
 #pragma unroll
         for (int j = 0; j < kOt; ++j) o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[j], o[a][j], 0, 0, 0);
         if (a + 1 < kOh) pa = pn;
-      }
+        // refill load u = a - 1 after head tile a (a = 1 .. kLHi)
+        constexpr int u = a - 1;
+        if constexpr (u >= 0 && u < kLHi) {
+          if (refill) {
+            if constexpr (u == 0) {
+              const int row = rrow < 0 ? (int)row0 : rrow;
+              rsrc = kv_bytes + (int64_t)row * kRowBytes + 16 * (opaque_lane_id() >> 5) + 32 * wave;
+            }
+            if (u < kLLo || hi) lds_dma16_imm<32 * NW * u>(rsrc, rtb + 1024 * NW * u);
+          }
+        }
+      });
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
 #pragma unroll
       for (int a = 0; a + 2 < kOh; ++a) {
