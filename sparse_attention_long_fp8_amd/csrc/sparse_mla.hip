@@ -409,7 +409,8 @@ static_assert(kColBytes * 2 == 1024, "a wave-wide load fills two chunk columns")
 
 struct MlaLds {
   uint8_t tile[kBufs][kTileBytes];
-  int32_t rows[kMaxSlots];  // resolved rows of the range (-1: masked slot)
+  int32_t rows[kMaxSlots];           // resolved rows of the range (-1: masked slot)
+  int32_t full[kMaxSlots / kBlk];    // tile has no masked slot
 };
 
 // 128 heads: the P.V product is split over output columns (see the kernel),
@@ -425,6 +426,7 @@ struct MlaXchg {
 struct MlaLdsSplit {
   uint8_t tile[kBufsSplit][kTileBytes];
   int32_t rows[kMaxSlots];
+  int32_t full[kMaxSlots / kBlk];
   MlaXchg x[2];      // exchange buffers of even and odd tiles
   float inv_l[128];  // 1 / denominator of each head
 };
@@ -511,11 +513,16 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
   }
   b = __builtin_amdgcn_readfirstlane(b);
   const int64_t row0 = key_row(kd, b, 0);  // stand-in row for masked / pad slots
-  // (4) resolve every slot of the range once
+  // (4) resolve every slot of the range once, and mark the tiles without a
+  // masked slot (a wave's 64 slots are two whole tiles)
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = tid + u * NT;
     if (i < nblk * kBlk) sh.rows[i] = sel[u] >= 0 ? (int32_t)key_row(kd, b, sel[u]) : -1;
+    const uint64_t valid = __ballot(sel[u] >= 0);
+    const int t0 = (64 * wave + u * NT) / kBlk;
+    if (lane == 0 && t0 < nblk) sh.full[t0] = (uint32_t)valid == 0xFFFFFFFFu;
+    if (lane == 0 && t0 + 1 < nblk) sh.full[t0 + 1] = (uint32_t)(valid >> 32) == 0xFFFFFFFFu;
   }
   lds_barrier();  // LDS only: the query loads stay in flight
 
@@ -615,24 +622,38 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * DSA_QK_AHEAD * HT, 1);
 
     // ---- online softmax (this lane: head n16 of each tile; tokens tok_of(4g+i), 16+tok_of(4g+i)) ----
-    bool ok[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ok[i] = rows[tok_of(4 * g + i)] >= 0;
-      ok[4 + i] = rows[16 + tok_of(4 * g + i)] >= 0;
-    }
+    // logits in the log2 domain; masked slots (only in tiles that have any)
+    // are -inf
     v8bf pf[HT];
     float alpha[HT];
     bool rescale = false;
     float z[HT][8], xl[HT];
     bool moves = false;  // some head's maximum may pass its reference by more than the slack
+    if (__builtin_amdgcn_readfirstlane(sh.full[blk])) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[ht][i] = s0[ht][i] * zscale;
+          z[ht][4 + i] = s1[ht][i] * zscale;
+        }
+    } else {
+      bool ok[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[ht][i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
-        z[ht][4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
+        ok[i] = rows[tok_of(4 * g + i)] >= 0;
+        ok[4 + i] = rows[16 + tok_of(4 * g + i)] >= 0;
       }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[ht][i] = ok[i] ? s0[ht][i] * zscale : -INFINITY;
+          z[ht][4 + i] = ok[4 + i] ? s1[ht][i] * zscale : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
       xl[ht] = z[ht][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) xl[ht] = fmaxf(xl[ht], z[ht][i]);
@@ -660,11 +681,13 @@ __global__ __launch_bounds__(NW * 64) void mla_bf16_kernel(
     }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const float m = m_ref[ht];
+      // a head with no reference yet has seen only masked slots: its terms
+      // are exp2(-inf) = 0 against any finite stand-in
+      const float m = m_ref[ht] == -INFINITY ? 0.f : m_ref[ht];
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pv = m == -INFINITY ? 0.f : fast_exp2(z[ht][i] - m);
+        const float pv = fast_exp2(z[ht][i] - m);
         sum += pv;
         pf[ht][i] = (__bf16)pv;
       }
