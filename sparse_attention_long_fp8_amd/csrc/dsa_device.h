@@ -83,6 +83,12 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score of an order-preserving key (inverse of float_key; +0 for the key
+// of +0 and -0).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // The lane index, computed where it is used: the compiler can neither hoist

@@ -570,11 +570,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
   // candidate lists of this wave's rows
   int cnt[QW];
   uint32_t tau[QW];
+  float tau_f[QW];  // the score whose key is tau (-inf while tau is 0)
   uint32_t klo[QW], khi[QW];  // this lane's bounds on the keys it appended (the list's: their wave min / max)
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     cnt[j] = 0;
     tau[j] = 0u;  // below every finite score's key
+    tau_f[j] = -INFINITY;
     klo[j] = 0xFFFFFFFFu;
     khi[j] = 0u;
   }
@@ -656,6 +658,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       __threadfence_block();
       cnt[j] = kept;
       tau[j] = th;
+      tau_f[j] = key_float(th);
       klo[j] = th;  // every kept key is at least the k-th
     }
   };
@@ -670,21 +673,28 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       if (cnt[j] + kTStageKeys > cap) select(j, false);
       float *cs = cand_s + (int64_t)row_t[j] * cap;
       int32_t *ci = cand_i + (int64_t)row_t[j] * cap;
+      // a stage wholly inside the row's history skips the per-key position test
+      auto append = [&](auto whole) __attribute__((always_inline)) {
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-        const int s = held_s0 + 32 * sub + col;
-        const uint32_t key = float_key(held[j][sub]);
-        const bool ok = half == 0 && s < row_n[j] && key > tau[j];
-        const uint64_t m = __ballot(ok);
-        if (ok) {
-          const int p = cnt[j] + lanes_below(m);
-          cs[p] = held[j][sub];
-          ci[p] = s;
-          klo[j] = min(klo[j], key);
-          khi[j] = max(khi[j], key);
+        for (int sub = 0; sub < kSub; ++sub) {
+          const int s = held_s0 + 32 * sub + col;
+          // key > tau, compared as floats: the key order is the order of the
+          // (finite) scores with -0 equal to +0, which float comparison keeps
+          const bool ok = half == 0 && (decltype(whole)::value || s < row_n[j]) && held[j][sub] > tau_f[j];
+          const uint64_t m = __ballot(ok);
+          if (ok) {
+            const uint32_t key = float_key(held[j][sub]);
+            const int p = cnt[j] + lanes_below(m);
+            cs[p] = held[j][sub];
+            ci[p] = s;
+            klo[j] = min(klo[j], key);
+            khi[j] = max(khi[j], key);
+          }
+          cnt[j] += __popcll(m);
         }
-        cnt[j] += __popcll(m);
-      }
+      };
+      if (held_s0 + kTStageKeys <= row_n[j]) append(std::true_type{});
+      else append(std::false_type{});
     }
   };
 
