@@ -673,19 +673,23 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       if (cnt[j] + kTStageKeys > cap) select(j, false);
       float *cs = cand_s + (int64_t)row_t[j] * cap;
       int32_t *ci = cand_i + (int64_t)row_t[j] * cap;
-      // a stage wholly inside the row's history skips the per-key position test
+      // A stage wholly inside the row's history skips the per-key position
+      // test.  Both half-waves hold every subtile's sums, so subtiles go in
+      // pairs: lanes 0-31 take subtile 2p, lanes 32-63 subtile 2p+1, whose
+      // keys all follow, so the ballot order is still position order.
       auto append = [&](auto whole) __attribute__((always_inline)) {
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
-          const int s = held_s0 + 32 * sub + col;
+        for (int sp = 0; sp < kSub / 2; ++sp) {
+          const float hv = half ? held[j][2 * sp + 1] : held[j][2 * sp];
+          const int s = held_s0 + 32 * (2 * sp + half) + col;
           // key > tau, compared as floats: the key order is the order of the
           // (finite) scores with -0 equal to +0, which float comparison keeps
-          const bool ok = half == 0 && (decltype(whole)::value || s < row_n[j]) && held[j][sub] > tau_f[j];
+          const bool ok = (decltype(whole)::value || s < row_n[j]) && hv > tau_f[j];
           const uint64_t m = __ballot(ok);
           if (ok) {
-            const uint32_t key = float_key(held[j][sub]);
+            const uint32_t key = float_key(hv);
             const int p = cnt[j] + lanes_below(m);
-            cs[p] = held[j][sub];
+            cs[p] = hv;
             ci[p] = s;
             klo[j] = min(klo[j], key);
             khi[j] = max(khi[j], key);
@@ -693,6 +697,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
           cnt[j] += __popcll(m);
         }
       };
+      static_assert(kSub % 2 == 0, "subtiles go in pairs");
       if (held_s0 + kTStageKeys <= row_n[j]) append(std::true_type{});
       else append(std::false_type{});
     }
