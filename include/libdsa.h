@@ -160,9 +160,8 @@ dsa_status_t dsa_topk_workspace_size(const dsa_batch_t *batch, int32_t k, size_t
  * cache, or in a paged one when max_k_len <= 131072 (each workgroup keeps
  * the page numbers of its sequence's history in LDS), for batches with
  * max_q_per_seq >= 8 (prefill, chunked prefill);
- * its workspace holds m*k + 128 candidates (rounded up to 64) of 8 bytes
- * per query row, m = 2 for max_k_len <= 4096 and one more per doubling of
- * max_k_len, at most 8 (m = 6 at 65536).  Other shapes run the two stages with the fp32 score rows in
+ * its workspace holds 3*k + 128 candidates (rounded up to 64) of 8 bytes
+ * per query row.  Other shapes run the two stages with the fp32 score rows in
  * the workspace, followed by dsa_topk's own workspace when it needs one.
  * Arguments as for the two stages; workspace 256-byte
  * aligned, dsa_indexer_topk_workspace_size() bytes.

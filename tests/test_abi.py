@@ -127,15 +127,14 @@ def test_workspace_sizes_and_too_small():
 
 def test_fused_indexer_topk_workspace_choice():
     """dsa_indexer_topk takes the fused kernel (candidate lists, 8 bytes per
-    entry, m*k + 128 entries rounded to 64 per row, m = 2 up to 4096 keys and
-    one more per doubling of the history, at most 8) for prefill batches with
-    contiguous keys or paged histories up to 131072 keys; past that, and for
-    decode batches, the two stages (fp32 score rows, then top-k's own)."""
+    entry, 3k + 128 entries rounded to 64 per row, whatever the history) for
+    prefill batches with contiguous keys or paged histories up to 131072 keys;
+    past that, and for decode batches, the two stages (fp32 score rows, then
+    top-k's own)."""
     k = 2048
 
     def cap(maxk):
-        m = {4096: 2, 4097: 3, 16384: 4, 65536: 6, 131072: 7, 140000: 8, 10 ** 6: 8}[maxk]
-        return (m * k + 128 + 63) // 64 * 64
+        return (3 * k + 128 + 63) // 64 * 64
 
     def r256(x):
         return -(-x // 256) * 256
@@ -158,7 +157,7 @@ def test_fused_indexer_topk_workspace_choice():
     assert ws(4096, 4096, 131072, True) == fused(131072)
     assert ws(4096, 4096, 131073, True) == unfused(4096, 4096, 131073)
     assert ws(4096, 4096, 140000, False) == fused(140000)     # contiguous keys: no length limit
-    assert ws(4096, 4096, 10 ** 6, False) == fused(10 ** 6)   # m stops at 8
+    assert ws(4096, 4096, 10 ** 6, False) == fused(10 ** 6)
     assert ws(32, 1, 32768, False) == unfused(32, 1, 32768)   # decode rows: the two stages
 
 
