@@ -363,6 +363,7 @@ struct IdxFusedLds {
   uint8_t keys[kTBufs][kTStageBytes];
   float ksc[kTBufs][kTStageKeys];
   uint32_t hist[4][256];  // one radix histogram per wave
+  int32_t want[2][4];     // wave w has a list near full (by stage parity)
   int32_t page[PAGED ? kFusedMaxPages : 1];
 };
 
@@ -696,11 +697,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
   // scores of the previous stage: appended to the lists at the start of the next one
   float held[QW][kSub];
   int held_s0 = 0;  // position of the held stage's key 0
-  auto emit_held = [&]() __attribute__((always_inline)) {
+  // A compaction holds up the other waves at the next stage barrier, so the
+  // waves compact together: before each barrier a wave flags whether one of
+  // its lists would fill within two stages, and after it, if any wave did,
+  // every wave compacts each of its lists that is over two thirds full (the
+  // waits then overlap).  A list that could overflow in this stage is compacted
+  // in any case.  `flags` is the stage parity the flags were written under.
+  auto emit_held = [&](int flags) __attribute__((always_inline)) {
+    const v4i wf = *(const v4i *)&sh.want[flags][0];
+    const bool together = (wf.x | wf.y | wf.z | wf.w) != 0;
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
       if (held_s0 >= row_n[j]) continue;  // uniform
-      if (cnt[j] + kTStageKeys > cap) select(j, false);
+      if (cnt[j] + kTStageKeys > cap || (together && 3 * cnt[j] > 2 * cap)) select(j, false);
       float *cs = cand_s + (int64_t)row_t[j] * cap;
       int32_t *ci = cand_i + (int64_t)row_t[j] * cap;
       // A stage wholly inside the row's history skips the per-key position
@@ -733,13 +742,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
     }
   };
 
+  if (tid < 8) sh.want[tid >> 2][tid & 3] = 0;
   for (int i = 0; i < kTBufs - 1 && i < nst; ++i) stage(i);
   wait_stages(min(kTBufs - 2, nst - 1));
   lds_barrier();
 
   for (int si = 0; si < nst; ++si) {
     const int buf = si % kTBufs;
-    if (si > 0) emit_held();
+    if (si > 0) emit_held((si - 1) & 1);
     if (si + kTBufs - 1 < nst) stage(si + kTBufs - 1);
     const int s_stage = si * kTStageKeys;
 #pragma unroll
@@ -757,10 +767,16 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_topk_fused_kernel(
       for (int j = 0; j < QW; ++j) held[j][sub] = sc[j];
     }
     held_s0 = s_stage;
+    // this wave's flag for the next stage's appends (stage si's keys, then
+    // stage si+1's): read after the barrier, rewritten two stages later
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < QW; ++j) near |= cnt[j] + 2 * kTStageKeys > cap;
+    if (lane == 0) sh.want[si & 1][wave] = near;
     wait_stages(min(si + kTBufs - 1, nst - 1) - (si + 1));
     lds_barrier();
   }
-  emit_held();
+  emit_held(nst > 0 ? (nst - 1) & 1 : 0);
 #pragma unroll
   for (int j = 0; j < QW; ++j)
     if (row_n[j] > 0) select(j, true);
