@@ -130,8 +130,13 @@ def fused_applies(wl, lay):
 
 
 def source_hash(stage):
-    path = os.path.join(ROOT, "sparse_attention_long_fp8_amd", "csrc", KERNEL_SOURCES[stage])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the stage's kernel source and of the device helpers every
+    kernel includes: a change to either invalidates the stage's counters."""
+    csrc = os.path.join(ROOT, "sparse_attention_long_fp8_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[stage], "dsa_device.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_of(stage, workload):

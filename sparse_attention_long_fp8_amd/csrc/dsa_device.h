@@ -18,6 +18,9 @@ struct BatchDev {
   int32_t num_seqs;
   const int32_t *q_seq_start;  // [B+1]
   const int32_t *k_len;        // [B]
+  // every sequence has exactly one query row (q_seq_start[b] == b, the
+  // decode batch): row t is sequence t, and its candidates are k_len[t]
+  int32_t one_per_seq;
 };
 
 // Key addressing: contiguous rows or 64-token pages.
@@ -33,6 +36,7 @@ constexpr int kPageSize = 1 << kPageShift;
 
 // Sequence that owns query row t: the largest b with q_seq_start[b] <= t.
 __device__ __forceinline__ int seq_of_row(const BatchDev &bt, int t) {
+  if (bt.one_per_seq) return t;
   int lo = 0, hi = bt.num_seqs - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -47,6 +51,7 @@ __device__ __forceinline__ int seq_of_row(const BatchDev &bt, int t) {
 // binary search pays one per halving).  Entries are non-decreasing; the
 // result is wave-uniform and in [0, num_seqs) for any array contents.
 __device__ __forceinline__ int seq_of_row_wave(const BatchDev &bt, int t) {
+  if (bt.one_per_seq) return t;
   const int lane = __lane_id();
   int b = 0;
   for (int span = bt.num_seqs; span > 1;) {
@@ -63,6 +68,7 @@ __device__ __forceinline__ int seq_of_row_wave(const BatchDev &bt, int t) {
 // Query row t of sequence b sits at p = k_len[b] - nq_b + (t - q_seq_start[b])
 // and has n = p + 1 causal candidates (itself included).
 __device__ __forceinline__ int candidates_of_row(const BatchDev &bt, int b, int t) {
+  if (bt.one_per_seq) return bt.k_len[b];
   int q0 = bt.q_seq_start[b];
   int nq = bt.q_seq_start[b + 1] - q0;
   return bt.k_len[b] - nq + (t - q0) + 1;

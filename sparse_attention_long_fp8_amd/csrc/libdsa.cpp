@@ -76,7 +76,12 @@ dsa_status_t check_layout(const dsa_kv_layout_t *ly, const dsa_batch_t *bt, cons
   return DSA_OK;
 }
 
-dsa::BatchDev to_dev(const dsa_batch_t *bt) { return dsa::BatchDev{bt->num_seqs, bt->q_seq_start, bt->k_len}; }
+// A batch whose every sequence has exactly one query row (the declared counts
+// allow nothing else) lets the kernels skip the sequence search.
+dsa::BatchDev to_dev(const dsa_batch_t *bt) {
+  const int one = bt->num_queries == bt->num_seqs && bt->max_q_per_seq == 1;
+  return dsa::BatchDev{bt->num_seqs, bt->q_seq_start, bt->k_len, one};
+}
 
 dsa::KeysDev to_dev(const dsa_kv_layout_t *ly) {
   return dsa::KeysDev{ly->paged, ly->k_seq_start, ly->page_table, ly->page_table_stride};
