@@ -109,7 +109,12 @@ def kernel_name(stage, wl, lay):
             return "indexer_f32_kernel"
         return "indexer_fp8_tiled_kernel" if lay.max_q_per_seq >= 8 else "indexer_fp8_staged_kernel"
     if stage == "topk":
-        return "topk_kernel"
+        # rows loaded before their length is known: decode batches (one query
+        # row per sequence) selected in one pass (not past 32768 keys in a
+        # batch of fewer than 256 rows)
+        two_pass = lay.num_queries < 256 and lay.max_k_len > 32768
+        one_per_seq = lay.num_queries == wl.batch and lay.max_q_per_seq == 1
+        return "topk_kernel<true>" if one_per_seq and not two_pass else "topk_kernel<false>"
     if not wl.fp8:
         return "mla_f32_kernel"
     # the bf16 launcher's split count: about one workgroup per CU, at least four

@@ -136,6 +136,7 @@ struct TopkSplit {
   int32_t *cpos;    // [T, ld_c] candidate positions
   float *cval;      // [T, ld_c] candidate scores
   int64_t ld_c;     // list stride: >= the longest list, a multiple of 4
+  int32_t lim;      // max_k_len: reads of a score row stay below it (ld >= max_k_len)
 };
 
 // Length of row t's candidate list up to (not including) part p.
@@ -145,6 +146,7 @@ __device__ __forceinline__ int list_offset(int n_row, int k, int p) {
   return off;
 }
 
+template <bool EARLY>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
                                                          const float *__restrict__ scores,
                                                          int64_t ld, int k,
@@ -152,6 +154,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
                                                          TopkSplit sp) {
   __shared__ TopkLds sh;
   const int t = blockIdx.x;
+  // EARLY (decode rows: one query row per sequence, selected in one pass):
+  // the row's first sweep chunk is loaded before its length is known, so
+  // that the length lookup's memory round trip passes under it.  The loads
+  // stop at max_k_len, inside the row, and elements past the row's
+  // candidates are never used (every use below tests i < n).  Causal
+  // prefill rows and the parts of long rows are often far shorter than
+  // max_k_len: there such loads would read mostly unused scores, so the
+  // launcher takes the other instantiation.
+  float4 v0[kU];
+  if constexpr (EARLY) load_chunk(scores + (int64_t)t * ld, 0, min(sp.lim, kTkCache), v0);
   const int b = seq_of_row_wave(bt, t);
   const int n_row = candidates_of_row(bt, b, t);
   int n = n_row;
@@ -202,7 +214,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(BatchDev bt,
   float vmin = INFINITY, vmax = -INFINITY;
   for (int base = 0; base < n; base += kChunk) {
     float4 v[kU];
-    load_chunk(row, base, n, v);
+    if (EARLY && base == 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = v0[u];
+    } else {
+      load_chunk(row, base, n, v);
+    }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = base + 4 * (tid + u * kTkThreads);
@@ -611,20 +628,25 @@ hipError_t launch_topk(const BatchDev &bt, int num_queries, int max_k_len, const
                        int k, int32_t *indices, void *workspace, hipStream_t stream) {
   if (num_queries == 0) return hipSuccess;
   TopkSplit sp{};
+  sp.lim = max_k_len;
   sp.parts = topk_parts(num_queries, max_k_len);
   if (!sp.parts) {
-    hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k, indices,
-                       sp);
+    if (bt.one_per_seq)
+      hipLaunchKernelGGL(topk_kernel<true>, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k,
+                         indices, sp);
+    else
+      hipLaunchKernelGGL(topk_kernel<false>, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k,
+                         indices, sp);
     return hipGetLastError();
   }
   sp.ld_c = topk_list_ld(sp.parts, k, max_k_len);
   const size_t list = ((size_t)num_queries * sp.ld_c * 4 + 255) / 256 * 256;
   sp.cpos = (int32_t *)workspace;
   sp.cval = (float *)((char *)workspace + list);
-  hipLaunchKernelGGL(topk_kernel, dim3(num_queries, sp.parts), dim3(kTkThreads), 0, stream, bt, scores, ld, k,
+  hipLaunchKernelGGL(topk_kernel<false>, dim3(num_queries, sp.parts), dim3(kTkThreads), 0, stream, bt, scores, ld, k,
                      indices, sp);
   sp.merge = 1;
-  hipLaunchKernelGGL(topk_kernel, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k, indices,
+  hipLaunchKernelGGL(topk_kernel<false>, dim3(num_queries), dim3(kTkThreads), 0, stream, bt, scores, ld, k, indices,
                      sp);
   return hipGetLastError();
 }

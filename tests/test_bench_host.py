@@ -65,6 +65,12 @@ def test_kernel_labels():
     assert lab["prefill_16k"] == "mla_bf16_kernel" and lab["tiny_prefill"] == "mla_f32_kernel"
     wl = synth.WORKLOADS["decode_32k"]
     assert bench.kernel_name("indexer", wl, synth.make_layout(wl)) == "indexer_fp8_staged_kernel"
+    tk = {n: bench.kernel_name("topk", synth.WORKLOADS[n], synth.make_layout(synth.WORKLOADS[n]))
+          for n in ("decode_32k", "paged_decode", "prefill_16k")}
+    # decode rows in one pass load before their length is known; paged rows
+    # past 32768 keys take the two passes, prefill rows the general form
+    assert tk == {"decode_32k": "topk_kernel<true>", "paged_decode": "topk_kernel<false>",
+                  "prefill_16k": "topk_kernel<false>"}
 
 
 @pytest.mark.parametrize("n", ["2", "8"])
